@@ -1,0 +1,487 @@
+"""Pins for the float64 oracle (CPU only).
+
+Each test ties the oracle to something that is not the oracle: a dense library
+routine (torch SDPA), brute force in pure Python over the pool, closed forms
+of attention, and invariants the pages fix (permutation of physical blocks,
+copy-on-write sharing).  The planted-mistake tests at the end break one step of
+the oracle at a time and check that some pin fails.
+"""
+
+import json
+import math
+import os
+import struct
+from collections import defaultdict
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import paged_attention as pa
+from paged_kv_cache_291_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def raw(wl):
+    return (W.raw_numpy(wl.query), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+            wl.block_tables, wl.seq_lens)
+
+
+def ref(wl, seqs=None):
+    q, kc, vc, bt, sl = raw(wl)
+    return oracle.paged_decode_ref(q, kc, vc, bt, sl, wl.scale, wl.dtype, seqs=seqs)
+
+
+# ---------------------------------------------------------------- element decode
+
+def test_bf16_decode_known_values():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x3E20, 0x4049, 0x7F80, 0x0001], dtype=np.uint16)
+    got = oracle.decode_values(bits, "bf16")
+    want = [1.0, -2.0, 0.0, -0.0, 0.15625, 3.140625, math.inf, 2.0 ** -133]
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[3]) == -1.0
+
+
+def test_bf16_decode_matches_torch_and_struct():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, size=4096, dtype=np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]            # finite values only
+    got = oracle.decode_values(bits, "bf16")
+    t = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, t)
+    for b in bits[:64].tolist():
+        (v,) = struct.unpack(">f", struct.pack(">H", b) + b"\x00\x00")
+        assert oracle.decode_values(np.array([b], np.uint16), "bf16")[0] == v
+
+
+def test_f16_decode_known_values():
+    bits = np.array([0x3C00, 0x3555, 0xC400, 0x0001, 0x7BFF], dtype=np.uint16)
+    got = oracle.decode_values(bits, "f16")
+    assert got.tolist() == [1.0, 0.333251953125, -4.0, 2.0 ** -24, 65504.0]
+
+
+def test_f32_decode_exact():
+    x = np.array([1.5, -3.25, 1e-30], dtype=np.float32)
+    assert oracle.decode_values(x, "f32").tolist() == [float(v) for v in x]
+
+
+def test_decode_rejects_wrong_types():
+    with pytest.raises(TypeError):
+        oracle.decode_values(np.zeros(3, np.float32), "bf16")
+    with pytest.raises(ValueError):
+        oracle.decode_values(np.zeros(3, np.float32), "f8")
+
+
+def test_kv_head_mapping():
+    assert [oracle.kv_head_of(h, 32, 8) for h in range(32)] == [h // 4 for h in range(32)]
+    assert [oracle.kv_head_of(h, 8, 8) for h in range(8)] == list(range(8))
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+
+
+# ---------------------------------------------------------------- P1: identity table == dense SDPA
+
+def _identity_case(dtype, S=3, Hq=8, Hkv=2, D=16, BS=4, lens=(5, 12, 1), seed=1):
+    rng = np.random.default_rng(seed)
+    mb = max(-(-np.array(lens) // BS))
+    nb = S * mb
+    tdt = W.TORCH_DTYPES[dtype]
+    kc = torch.from_numpy(rng.standard_normal((nb, BS, Hkv, D)).astype(np.float32)).to(tdt)
+    vc = torch.from_numpy(rng.standard_normal((nb, BS, Hkv, D)).astype(np.float32)).to(tdt)
+    q = torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float32)).to(tdt)
+    bt = (np.arange(S)[:, None] * mb + np.arange(mb)[None, :]).astype(np.int32)
+    return q, kc, vc, bt, np.array(lens, np.int32), mb
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (8, 1)])
+def test_identity_table_equals_dense_sdpa(dtype, Hq, Hkv):
+    q, kc, vc, bt, lens, mb = _identity_case(dtype, Hq=Hq, Hkv=Hkv)
+    S, _, D = q.shape
+    BS = kc.shape[1]
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.paged_decode_ref(W.raw_numpy(q), W.raw_numpy(kc), W.raw_numpy(vc), bt, lens, scale, dtype)
+    G = Hq // Hkv
+    dense_k = kc.to(torch.float64).reshape(S, mb * BS, Hkv, D)   # contiguous per sequence
+    dense_v = vc.to(torch.float64).reshape(S, mb * BS, Hkv, D)
+    for s in range(S):
+        L = int(lens[s])
+        K = dense_k[s, :L].permute(1, 0, 2).repeat_interleave(G, dim=0)[None]  # [1, Hq, L, D]
+        V = dense_v[s, :L].permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        Q = q[s].to(torch.float64)[None, :, None, :]                            # [1, Hq, 1, D]
+        want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[0, :, 0, :]
+        assert np.max(np.abs(got[s] - want.numpy())) <= 1e-12
+
+
+# ---------------------------------------------------------------- P4: brute force over the pool
+
+def _bf16_to_float(b):
+    return struct.unpack(">f", struct.pack(">H", int(b) & 0xFFFF) + b"\x00\x00")[0]
+
+
+def _as_pyfloat(x, dtype):
+    if dtype == "bf16":
+        return _bf16_to_float(x)
+    return float(x)
+
+
+def brute_force(q, kc, vc, tables, lens, scale, dtype):
+    """Pure Python: walk the pool block by block through the inverse of the
+    block tables, collect each sequence's rows, then softmax attention with
+    math.exp and math.fsum."""
+    S, Hq, D = len(q), len(q[0]), len(q[0][0])
+    NB, BS, Hkv = len(kc), len(kc[0]), len(kc[0][0])
+    G = Hq // Hkv
+    users = defaultdict(list)                      # physical block -> [(seq, logical block)]
+    for s in range(S):
+        for j in range((int(lens[s]) + BS - 1) // BS):
+            users[int(tables[s][j])].append((s, j))
+    rows = {}                                      # (s, t, kvh) -> (k row, v row)
+    for b in range(NB):
+        for (s, j) in users.get(b, []):
+            for off in range(BS):
+                t = j * BS + off
+                if t < int(lens[s]):
+                    for kvh in range(Hkv):
+                        rows[(s, t, kvh)] = ([_as_pyfloat(x, dtype) for x in kc[b][off][kvh]],
+                                             [_as_pyfloat(x, dtype) for x in vc[b][off][kvh]])
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(S)]
+    for s in range(S):
+        L = int(lens[s])
+        for h in range(Hq):
+            if L == 0:
+                continue
+            kvh = h // G
+            qh = [_as_pyfloat(x, dtype) for x in q[s][h]]
+            z = [scale * math.fsum(qh[d] * rows[(s, t, kvh)][0][d] for d in range(D)) for t in range(L)]
+            m = max(z)
+            e = [math.exp(zt - m) for zt in z]
+            den = math.fsum(e)
+            for d in range(D):
+                out[s][h][d] = math.fsum(e[t] * rows[(s, t, kvh)][1][d] for t in range(L)) / den
+    return out
+
+
+def _tiny(dtype, Hq, Hkv, BS, lens, seed, tables=None, nb=None):
+    rng = np.random.default_rng(seed)
+    D = 4
+    lens = np.asarray(lens, np.int32)
+    nblk = -(-lens // BS)
+    if tables is None:
+        nb = int(nblk.sum()) + 3
+        perm = rng.permutation(nb)
+        tables = W._tables_from_ids(perm, nblk, max(1, int(nblk.max())))
+    tdt = W.TORCH_DTYPES[dtype]
+    kc = torch.from_numpy(rng.standard_normal((nb, BS, Hkv, D)).astype(np.float32)).to(tdt)
+    vc = torch.from_numpy(rng.standard_normal((nb, BS, Hkv, D)).astype(np.float32)).to(tdt)
+    q = torch.from_numpy(rng.standard_normal((len(lens), Hq, D)).astype(np.float32)).to(tdt)
+    return W.raw_numpy(q), W.raw_numpy(kc), W.raw_numpy(vc), tables, lens
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (4, 2), (2, 2)])
+@pytest.mark.parametrize("BS,lens", [(2, (1, 2, 3)), (2, (5, 16, 17)), (16, (1, 17, 16))])
+def test_brute_force_tiny(dtype, Hq, Hkv, BS, lens):
+    q, kc, vc, bt, sl = _tiny(dtype, Hq, Hkv, BS, lens, seed=Hq * 7 + BS + len(lens))
+    scale = 0.5
+    got = oracle.paged_decode_ref(q, kc, vc, bt, sl, scale, dtype)
+    want = np.array(brute_force(q.tolist(), kc.tolist(), vc.tolist(), bt.tolist(), sl, scale, dtype))
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+@pytest.mark.parametrize("BS", [2, 16])
+def test_brute_force_block_pool_figure(BS):
+    fig = json.load(open(os.path.join(GOLDEN, "block_pool_figure.json")))
+    names = ["A", "B", "C"]
+    mb = max(len(fig["tables"][n]) for n in names)
+    tables = np.full((3, mb), -1, np.int32)
+    for i, n in enumerate(names):
+        tables[i, :len(fig["tables"][n])] = fig["tables"][n]
+    lens = [fig[f"seq_lens_block_size_{BS}"][n] for n in names]
+    q, kc, vc, bt, sl = _tiny("f32", 4, 2, BS, lens, seed=BS, tables=tables, nb=fig["num_blocks"])
+    kc[0] = np.nan                                   # block 0 is named by no table
+    vc[0] = np.nan
+    got = oracle.paged_decode_ref(q, kc, vc, bt, sl, 0.5, "f32")
+    want = np.array(brute_force(q.tolist(), kc.tolist(), vc.tolist(), bt.tolist(), sl, 0.5, "f32"))
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got - want)) <= 1e-12
+
+
+# ---------------------------------------------------------------- P2, P3: invariants
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_permutation_invariance(dtype):
+    wl = W.make_random(3, 4, 8, 2, 32, dtype, [1, 16, 33, 70], block_size=16, pool_factor=2.0)
+    wp = W.permute_blocks(wl, seed=5)
+    assert not np.array_equal(wl.block_tables, wp.block_tables)
+    assert np.array_equal(ref(wl), ref(wp))
+
+
+def test_cow_shared_prefix_equals_private_copies():
+    rng = np.random.default_rng(11)
+    S, pb, bs = 5, 3, 16
+    tails = rng.integers(1, 40, size=S)
+    lens = (pb * bs + tails).astype(np.int32)
+    tail_blk = -(-tails // bs)
+    nb = pb + int(tail_blk.sum()) + 2
+    perm = rng.permutation(nb)
+    tables = np.full((S, pb + int(tail_blk.max())), -1, np.int32)
+    tables[:, :pb] = perm[:pb]
+    tables[:, pb:] = W._tables_from_ids(perm[pb:], tail_blk, int(tail_blk.max()))
+    wl = W.build("cow", "bf16", lens, tables, nb, 8, 2, 32, bs, rng, poison=True,
+                 shared_prefix_tokens=pb * bs)
+    wp = W.unshare_prefix(wl, pb)
+    assert len(set(wp.block_tables[:, :pb].ravel().tolist())) == S * pb
+    a, b = ref(wl), ref(wp)
+    assert np.isfinite(a).all()
+    assert np.array_equal(a, b)
+
+
+def test_unreferenced_blocks_never_read():
+    wl = W.make_random(4, 3, 4, 2, 16, "f32", [7, 16, 31], pool_factor=3.0)
+    out = ref(wl)                    # pool is NaN outside the named rows
+    assert np.isfinite(out).all()
+
+
+# ---------------------------------------------------------------- P5: softmax rows
+
+def test_softmax_rows_sum_to_one():
+    wl = W.make_random(6, 3, 8, 2, 32, "bf16", [1, 45, 300])
+    q, kc, vc, bt, sl = raw(wl)
+    for s in range(3):
+        for h in range(8):
+            p = oracle.paged_decode_probs_ref(q, kc, vc, bt, sl, wl.scale, wl.dtype, s, h)
+            assert len(p) == sl[s]
+            assert (p >= 0).all()
+            assert abs(p.sum() - 1.0) <= 1e-12
+
+
+# ---------------------------------------------------------------- P6: closed forms
+
+def _one_seq(K, V, q, BS=4, dtype="f32"):
+    L, D = K.shape
+    nblk = -(-L // BS)
+    kc = np.full((nblk + 1, BS, 1, D), np.nan, np.float32)
+    vc = np.full((nblk + 1, BS, 1, D), np.nan, np.float32)
+    order = np.arange(nblk)[::-1] + 1              # reversed physical order
+    for t in range(L):
+        kc[order[t // BS], t % BS, 0] = K[t]
+        vc[order[t // BS], t % BS, 0] = V[t]
+    bt = order[None, :].astype(np.int32)
+    return q[None, None, :].astype(np.float32), kc, vc, bt, np.array([L], np.int32)
+
+
+def test_single_token_returns_its_value_exactly():
+    rng = np.random.default_rng(2)
+    K = rng.standard_normal((1, 8)).astype(np.float32)
+    V = rng.standard_normal((1, 8)).astype(np.float32)
+    q = rng.standard_normal(8).astype(np.float32)
+    out = oracle.paged_decode_ref(*_one_seq(K, V, q), 0.37, "f32")
+    assert out[0, 0].tolist() == V[0].astype(np.float64).tolist()
+
+
+def test_zero_query_gives_mean_of_values():
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((13, 8)).astype(np.float32)
+    V = rng.standard_normal((13, 8)).astype(np.float32)
+    out = oracle.paged_decode_ref(*_one_seq(K, V, np.zeros(8, np.float32)), 0.5, "f32")
+    assert np.max(np.abs(out[0, 0] - V.astype(np.float64).mean(0))) <= 1e-12
+
+
+def test_equal_keys_give_mean_of_values():
+    rng = np.random.default_rng(4)
+    K = np.tile(rng.standard_normal((1, 8)).astype(np.float32), (9, 1))
+    V = rng.standard_normal((9, 8)).astype(np.float32)
+    q = rng.standard_normal(8).astype(np.float32)
+    out = oracle.paged_decode_ref(*_one_seq(K, V, q), 0.5, "f32")
+    assert np.max(np.abs(out[0, 0] - V.astype(np.float64).mean(0))) <= 1e-12
+
+
+def test_dominant_key_selects_its_value():
+    rng = np.random.default_rng(5)
+    K = (0.01 * rng.standard_normal((11, 8))).astype(np.float32)
+    q = rng.standard_normal(8).astype(np.float32)
+    K[6] = 64.0 * q                                  # z_6 exceeds the rest by > 100
+    V = rng.standard_normal((11, 8)).astype(np.float32)
+    out = oracle.paged_decode_ref(*_one_seq(K, V, q), 1.0, "f32")
+    assert np.max(np.abs(out[0, 0] - V[6].astype(np.float64))) <= 1e-12
+
+
+def test_two_tokens_logistic_weights():
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((2, 8)).astype(np.float32)
+    V = rng.standard_normal((2, 8)).astype(np.float32)
+    q = rng.standard_normal(8).astype(np.float32)
+    scale = 0.3
+    z0 = scale * math.fsum(float(a) * float(b) for a, b in zip(q, K[0]))
+    z1 = scale * math.fsum(float(a) * float(b) for a, b in zip(q, K[1]))
+    w0 = 1.0 / (1.0 + math.exp(z1 - z0))             # logistic function of the score gap
+    want = w0 * V[0].astype(np.float64) + (1.0 - w0) * V[1].astype(np.float64)
+    out = oracle.paged_decode_ref(*_one_seq(K, V, q), scale, "f32")
+    assert np.max(np.abs(out[0, 0] - want)) <= 1e-12
+
+
+def test_scale_equivariance():
+    rng = np.random.default_rng(7)
+    K = rng.standard_normal((21, 8)).astype(np.float32)
+    V = rng.standard_normal((21, 8)).astype(np.float32)
+    q = rng.standard_normal(8).astype(np.float32)
+    a = oracle.paged_decode_ref(*_one_seq(K, V, q), 0.5, "f32")
+    b = oracle.paged_decode_ref(*_one_seq(K, V, 4.0 * q), 0.125, "f32")
+    c = oracle.paged_decode_ref(*_one_seq(K, V, q), 2.0, "f32")
+    assert np.array_equal(a, b)
+    assert np.max(np.abs(a - c)) > 1e-3              # the scale does change the result
+
+
+def test_output_is_convex_combination_of_values():
+    wl = W.make_random(8, 4, 8, 2, 32, "bf16", [3, 17, 64, 200])
+    q, kc, vc, bt, sl = raw(wl)
+    out = ref(wl)
+    for s in range(4):
+        for h in range(8):
+            V = oracle.decode_values(oracle.gather_rows(vc, bt[s], sl[s], h // 4), "bf16")
+            assert (out[s, h] <= V.max(0) + 1e-12).all() and (out[s, h] >= V.min(0) - 1e-12).all()
+
+
+def test_empty_sequence_gives_zero():
+    wl = W.make_random(9, 3, 4, 4, 16, "f32", [0, 5, 0])
+    out = ref(wl)
+    assert (out[0] == 0).all() and (out[2] == 0).all() and np.isfinite(out[1]).all()
+
+
+# ---------------------------------------------------------------- P7: split + LSE algebra
+
+@pytest.mark.parametrize("ps", [1, 16, 32, 512, 4096])
+def test_partition_lse_combine_equals_direct(ps):
+    wl = W.make_random(10, 4, 8, 2, 32, "bf16", [1, 100, 513, 1100])
+    q, kc, vc, bt, sl = raw(wl)
+    direct = ref(wl)
+    parts = oracle.paged_decode_partials_ref(q, kc, vc, bt, sl, wl.scale, wl.dtype, ps)
+    for s in range(4):
+        for h in range(8):
+            plist = parts[(s, h)]
+            assert len(plist) == -(-int(sl[s]) // ps)
+            got = oracle.lse_combine_ref(plist, 32)
+            assert np.max(np.abs(got - direct[s, h])) <= 1e-12
+
+
+def test_lse_combine_no_partitions():
+    assert (oracle.lse_combine_ref([], 8) == 0).all()
+
+
+# ---------------------------------------------------------------- P8: scatter
+
+def _scatter_loop(key, value, kc, vc, slots):
+    kc, vc = kc.copy(), vc.copy()
+    NB, BS, H, D = kc.shape
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, o = slot // BS, slot % BS
+        for h in range(H):
+            for d in range(D):
+                kc[b, o, h, d] = key[i, h, d]
+                vc[b, o, h, d] = value[i, h, d]
+    return kc, vc
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_scatter_matches_elementwise_loop(dtype):
+    rng = np.random.default_rng(12)
+    NB, BS, H, D, T = 6, 4, 2, 8, 7
+    tdt = W.TORCH_DTYPES[dtype]
+    mk = lambda *s: W.raw_numpy(torch.from_numpy(rng.standard_normal(s).astype(np.float32)).to(tdt))
+    kc, vc, key, value = mk(NB, BS, H, D), mk(NB, BS, H, D), mk(T, H, D), mk(T, H, D)
+    slots = rng.choice(NB * BS, size=T, replace=False).astype(np.int32)
+    slots[2] = -1
+    slots[5] = -7
+    gk, gv = oracle.reshape_and_cache_ref(key, value, kc, vc, slots)
+    wk, wv = _scatter_loop(key, value, kc, vc, slots)
+    assert gk.tobytes() == wk.tobytes() and gv.tobytes() == wv.tobytes()
+    written = np.zeros(NB * BS, bool)
+    written[slots[slots >= 0]] = True
+    flat_old, flat_new = kc.reshape(NB * BS, -1), gk.reshape(NB * BS, -1)
+    assert flat_old[~written].tobytes() == flat_new[~written].tobytes()
+    assert kc.tobytes() != gk.tobytes()
+
+
+def test_scatter_then_gather_round_trip():
+    wl = W.make_random(13, 3, 4, 2, 16, "bf16", [5, 16, 20])
+    q, kc, vc, bt, sl = raw(wl)
+    rng = np.random.default_rng(0)
+    key = rng.integers(-30000, 30000, size=(3, 2, 16)).astype(np.int16)
+    value = rng.integers(-30000, 30000, size=(3, 2, 16)).astype(np.int16)
+    slots = np.array([bt[s, (sl[s] - 1) // 16] * 16 + (sl[s] - 1) % 16 for s in range(3)], np.int32)
+    kc2, vc2 = oracle.reshape_and_cache_ref(key, value, kc, vc, slots)
+    for s in range(3):
+        for kvh in range(2):
+            assert (oracle.gather_rows(kc2, bt[s], sl[s], kvh)[-1] == key[s, kvh]).all()
+            assert (oracle.gather_rows(vc2, bt[s], sl[s], kvh)[-1] == value[s, kvh]).all()
+
+
+# ---------------------------------------------------------------- planted mistakes must fail a pin
+
+def _p1_ok():
+    try:
+        for dtype in ("f32",):
+            test_identity_table_equals_dense_sdpa(dtype, 8, 2)
+        return True
+    except AssertionError:
+        return False
+
+
+def _p4_ok():
+    try:
+        test_brute_force_tiny("f32", 4, 2, 2, (5, 16, 17))
+        return True
+    except AssertionError:
+        return False
+
+
+def test_pins_pass_unmodified():
+    assert _p1_ok() and _p4_ok()
+
+
+def test_planted_wrong_head_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(pa, "kv_head_of", lambda h, hq, hkv: h % hkv)
+    assert not _p1_ok() and not _p4_ok()
+
+
+def test_planted_wrong_token_offset_is_caught(monkeypatch):
+    orig = pa.gather_rows
+
+    def shifted(cache, table_row, seq_len, kv_head):
+        bs = cache.shape[1]
+        t = np.arange(int(seq_len))
+        return np.asarray(cache)[np.asarray(table_row)[t // bs], (t + 1) % bs, kv_head, :]
+
+    monkeypatch.setattr(pa, "gather_rows", shifted)
+    assert not _p1_ok() and not _p4_ok()
+    monkeypatch.setattr(pa, "gather_rows", orig)
+    assert _p1_ok()
+
+
+def test_planted_dropped_scale_is_caught(monkeypatch):
+    orig = pa.softmax_attention
+    monkeypatch.setattr(pa, "softmax_attention", lambda q, K, V, scale: orig(q, K, V, 1.0))
+    assert not _p1_ok() and not _p4_ok()
+
+
+def test_planted_transposed_value_is_caught(monkeypatch):
+    orig = pa.softmax_attention
+
+    def bad(q, K, V, scale):
+        out, p = orig(q, K, V, scale)
+        return (p[::-1] @ V if len(p) > 1 else out), p
+
+    monkeypatch.setattr(pa, "softmax_attention", bad)
+    assert not _p1_ok() and not _p4_ok()
+
+
+def test_planted_missing_last_token_is_caught(monkeypatch):
+    orig = pa.gather_rows
+    monkeypatch.setattr(pa, "gather_rows",
+                        lambda c, t, L, h: orig(c, t, max(int(L) - 1, 1) if int(L) > 1 else L, h))
+    assert not _p1_ok() and not _p4_ok()
