@@ -1,0 +1,129 @@
+/*
+ * pagedattn.h - C ABI of the MI355X (gfx950) paged decode attention library.
+ *
+ * The operation (devpress.csdn.net article on the vLLM architecture,
+ * section 3 "PagedAttention kernel: from concept to CUDA"):
+ *   part 1 gives the inputs: query[num_seqs, num_heads, head_size],
+ *     block_tables[num_seqs, max_blocks_per_seq] and one pool per cache,
+ *     k_cache/v_cache[num_physical_blocks, block_size, num_kv_heads, head_size];
+ *   part 2 gives the flow: for each sequence take its block table, its actual
+ *     length and the number of logical blocks, gather K/V from the physical
+ *     blocks the table names, run standard attention of the query over them,
+ *     write the output.
+ * A block holds the K/V of 16 tokens (aiflowlearn.net vLLM course page,
+ * section on cutting the KV cache into pages).
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees, keeps no global state, and is re-entrant.
+ *  - Tensors are dense and row-major in the shapes given; q, caches and
+ *    outputs share one element type (enum pa_dtype).  Data pointers must be
+ *    16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work on it; there is no host synchronisation.
+ *  - Errors that the host can see (null pointer, unsupported size or type,
+ *    bad partition size, workspace too small, misalignment) are returned
+ *    synchronously and nothing is launched.  A launch failure returns
+ *    PA_ERR_HIP.  Device-side contract violations never fault: a sequence
+ *    whose length is negative or exceeds max_blocks_per_seq * block_size, or
+ *    whose first ceil(len / block_size) table entries are not all in
+ *    [0, num_blocks), gets NaN in its output rows instead.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad shape relation, misalignment */
+  PA_ERR_UNSUPPORTED = -2,  /* dtype / head_size / block_size / group size not built        */
+  PA_ERR_WORKSPACE = -3,    /* split path without a large enough workspace                   */
+  PA_ERR_HIP = -4           /* the HIP runtime reported an error at launch                   */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Human-readable name of a pa_status value (static string, never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * Bytes of device workspace the split-context path needs:
+ *   num_seqs * num_heads * ceil(max_seq_len / partition_size) * (head_size + 2) * 4
+ * (fp32 partial outputs plus a max and a sum per partition).  Returns 0 when
+ * partition_size <= 0 (single pass) and also for invalid sizes.
+ * max_seq_len must be the value later passed to paged_attention_decode, or
+ * max_blocks_per_seq * block_size if 0 is passed there.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
+                                int max_seq_len, int partition_size);
+
+/*
+ * Paged decode attention: one new query token per (sequence, head).
+ *
+ *   out[s, h, :] = sum_t softmax_t(scale * <query[s, h, :], K_t>) * V_t
+ *
+ * over the tokens t < seq_lens[s] of sequence s, where token t of KV head
+ * g = h / (num_heads / num_kv_heads) is row
+ *   k_cache[block_tables[s, t / block_size], t % block_size, g, :]
+ * (and likewise for v_cache).  seq_lens[s] == 0 gives a zero output row.
+ *
+ *  out            [num_seqs, num_heads, head_size], written (dtype)
+ *  query          [num_seqs, num_heads, head_size] (dtype)
+ *  k_cache        [num_blocks, block_size, num_kv_heads, head_size] (dtype)
+ *  v_cache        same shape and dtype as k_cache
+ *  block_tables   int32 [num_seqs, max_blocks_per_seq]; only the first
+ *                 ceil(seq_lens[s] / block_size) entries of row s are read
+ *  seq_lens       int32 [num_seqs]
+ *  head_size      64 or 128;  block_size: 16
+ *  num_heads / num_kv_heads must be 1, 2, 4 or 8 (grouped-query attention)
+ *  max_seq_len    upper bound on seq_lens (sizes the split grid and the
+ *                 workspace); 0 means max_blocks_per_seq * block_size
+ *  scale          softmax scale (usually 1/sqrt(head_size))
+ *  dtype          pa_dtype of query, caches and out
+ *  partition_size 0: one pass per (sequence, kv head).
+ *                 > 0: split context into partitions of this many tokens (a
+ *                 multiple of block_size); a second kernel merges partitions
+ *                 with log-sum-exp weights.  Needs `workspace`.
+ *  workspace      device buffer of >= pa_decode_workspace_size(...) bytes,
+ *                 256-byte aligned, used only when partition_size > 0
+ *                 (may be NULL otherwise).  Its contents are scratch.
+ */
+int paged_attention_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                           int block_size, int max_blocks_per_seq, int num_blocks,
+                           int max_seq_len, float scale, int dtype, int partition_size,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Scatter new tokens' K/V rows into their cache slots (csdn article,
+ * section 4 point 3: gather-scatter in place of contiguous access; section 2
+ * part 4: a new token joins its sequence's blocks).
+ *
+ *   for i < num_tokens with 0 <= slot_mapping[i] < num_blocks * block_size:
+ *     k_cache[slot / block_size, slot % block_size, :, :] = key[i, :, :]
+ *     v_cache[slot / block_size, slot % block_size, :, :] = value[i, :, :]
+ *
+ * Bytes are copied unchanged (bit-exact).  Negative slots mean "no write";
+ * slots at or past num_blocks * block_size are skipped too.  Two tokens must
+ * not share a slot (which write wins is then unspecified).
+ *
+ *  key, value       [num_tokens, num_kv_heads, head_size] (dtype)
+ *  k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size], updated in place
+ *  slot_mapping     int32 [num_tokens]
+ */
+int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                      int head_size, int block_size, int num_blocks, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

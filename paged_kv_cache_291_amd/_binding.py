@@ -1,0 +1,146 @@
+"""ctypes binding of libpagedattn.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(``include/pagedattn.h``).  There is no CPU fallback: if the library is not
+built, or a tensor is not on a HIP device, the call raises.  PyTorch is used
+for device memory and the current stream only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache")
+
+_lib = None
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with paged_kv_cache_291_amd/build.py "
+                           "(no CPU fallback exists)")
+    lib = ctypes.CDLL(p)
+    c_int, c_size, vp, c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [c_int]
+    lib.pa_decode_workspace_size.restype = c_size
+    lib.pa_decode_workspace_size.argtypes = [c_int] * 5
+    lib.paged_attention_decode.restype = c_int
+    lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
+                                           c_int, c_int, c_int, c_float, c_int, c_int, vp, c_size, vp]
+    lib.reshape_and_cache.restype = c_int
+    lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def _check(rc: int):
+    if rc != PA_OK:
+        raise PagedAttnError(rc, pa_status_string(rc))
+
+
+def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_size: int, max_seq_len: int,
+                             partition_size: int) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, head_size, max_seq_len,
+                                                       partition_size))
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                           scale: float, partition_size: int = 0, max_seq_len: int = 0,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Enqueue paged decode attention on ``stream`` (default: torch's current stream).
+
+    Shapes: out/query ``[S, Hq, D]``; caches ``[NB, BS, Hkv, D]``;
+    block_tables int32 ``[S, max_blocks]``; seq_lens int32 ``[S]``.
+    With ``partition_size > 0`` a workspace is needed: pass one (uint8 device
+    tensor, 256-byte aligned) or let this wrapper allocate it.
+    """
+    S, Hq, D = query.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between out/query/k_cache/v_cache")
+    if query.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {query.dtype}")
+    dt = query.dtype
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and seq_lens [S]")
+    ws_ptr, ws_bytes = 0, 0
+    if partition_size > 0:
+        msl = max_seq_len if max_seq_len > 0 else block_tables.shape[1] * BS
+        need = pa_decode_workspace_size(S, Hq, D, msl, partition_size)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    rc = load_library().paged_attention_decode(
+        _dev(out, "out", dt), _dev(query, "query", dt), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), _dev(block_tables, "block_tables", torch.int32),
+        _dev(seq_lens, "seq_lens", torch.int32), S, Hq, Hkv, D, BS, block_tables.shape[1], NB,
+        int(max_seq_len), float(scale), DTYPE_CODES[dt], int(partition_size), ws_ptr, ws_bytes,
+        _stream(stream))
+    _check(rc)
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Enqueue the scatter of ``key``/``value`` ``[T, Hkv, D]`` into their cache slots."""
+    T, Hkv, D = key.shape
+    NB, BS, Hkv2, D2 = k_cache.shape
+    if tuple(value.shape) != (T, Hkv, D) or (Hkv2, D2) != (Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between key/value and the caches")
+    if key.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {key.dtype}")
+    dt = key.dtype
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    rc = load_library().reshape_and_cache(
+        _dev(key, "key", dt), _dev(value, "value", dt), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), _dev(slot_mapping, "slot_mapping", torch.int32), T, Hkv, D, BS,
+        NB, DTYPE_CODES[dt], _stream(stream))
+    _check(rc)

@@ -27,6 +27,8 @@ drawn in a fixed order: seq_lens, block permutation, slot targets, q, k, v.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Optional
 
@@ -35,7 +37,7 @@ import torch
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-_CHUNK = 1 << 24  # float32 values per draw chunk (64 MiB)
+_CHUNK = 1 << 24  # values per draw chunk
 
 
 @dataclass
@@ -93,12 +95,36 @@ def _rng(cfg: int, seed: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([291, cfg, seed]))
 
 
+def _workers() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 def _normal(rng: np.random.Generator, shape, dtype: str) -> torch.Tensor:
+    """N(0, 1) values, drawn in float32 chunks of 2^24 and rounded to ``dtype``.
+
+    One 64-bit key is taken from ``rng``; chunk i is drawn from its own stream
+    ``SeedSequence([key, i])``, so the values depend on the seed only, not on
+    how many threads draw them.
+    """
     n = int(np.prod(shape))
     out = torch.empty(n, dtype=TORCH_DTYPES[dtype])
-    for a in range(0, n, _CHUNK):
-        b = min(n, a + _CHUNK)
-        out[a:b] = torch.from_numpy(rng.standard_normal(b - a, dtype=np.float32)).to(out.dtype)
+    key = int(rng.integers(0, 2 ** 63))
+
+    def fill(i):
+        a, b = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        g = np.random.default_rng(np.random.SeedSequence([key, i]))
+        out[a:b] = torch.from_numpy(g.standard_normal(b - a, dtype=np.float32)).to(out.dtype)
+
+    nchunks = -(-n // _CHUNK)
+    if nchunks <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.view(*shape)
 
 
@@ -121,11 +147,8 @@ def _fill_pool(rng, dtype, num_blocks, bs, hkv, d, slots: np.ndarray, poison: bo
     tdt = TORCH_DTYPES[dtype]
     pool = (torch.full if poison else lambda shape, v, dtype: torch.zeros(shape, dtype=dtype))(
         (num_blocks * bs, hkv, d), float("nan"), dtype=tdt)
-    rows_per_chunk = max(1, _CHUNK // (hkv * d))
-    idx = torch.from_numpy(slots)
-    for a in range(0, len(slots), rows_per_chunk):
-        b = min(len(slots), a + rows_per_chunk)
-        pool.index_copy_(0, idx[a:b], _normal(rng, (b - a, hkv, d), dtype))
+    if len(slots):
+        pool.index_copy_(0, torch.from_numpy(slots), _normal(rng, (len(slots), hkv, d), dtype))
     return pool.view(num_blocks, bs, hkv, d)
 
 
