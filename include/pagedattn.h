@@ -22,7 +22,7 @@
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
  *    enqueue work on it; there is no host synchronisation.
  *  - Errors that the host can see (null pointer, unsupported size or type,
- *    bad partition size, workspace too small, misalignment) are returned
+ *    bad partition size or flags, workspace too small, misalignment) are returned
  *    synchronously and nothing is launched.  A launch failure returns
  *    PA_ERR_HIP.  Device-side contract violations never fault: a sequence
  *    whose length is negative or exceeds max_blocks_per_seq * block_size, or
@@ -49,16 +49,29 @@ typedef enum {
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
+/* Flags of paged_attention_decode. */
+enum {
+  /* Physical blocks may be named by several sequences of the batch (shared
+   * prefixes, copy-on-write): read K/V with the default cache policy so a
+   * shared block stays cached for its other readers.  Without the flag K/V
+   * are streamed with non-temporal loads (each block is read once per call). */
+  PA_FLAG_SHARED_BLOCKS = 1
+};
+
 /* Human-readable name of a pa_status value (static string, never NULL). */
 const char* pa_status_string(int status);
 
 /*
- * Bytes of device workspace the split-context path needs:
- *   num_seqs * num_heads * ceil(max_seq_len / partition_size) * (head_size + 2) * 4
- * (fp32 partial outputs plus a max and a sum per partition).  Returns 0 when
- * partition_size <= 0 (single pass) and also for invalid sizes.
- * max_seq_len must be the value later passed to paged_attention_decode, or
- * max_blocks_per_seq * block_size if 0 is passed there.
+ * Bytes of device workspace paged_attention_decode needs (an upper bound):
+ *  partition_size > 0:
+ *    num_seqs * num_heads * ceil(max_seq_len / partition_size) * (head_size + 4) * 4
+ *    (one fp32 partial record per partition: max, sum, 2 unused, output)
+ *  partition_size == 0 (balanced split, bf16/fp16 KV):
+ *    round_up((num_seqs + 1) * 4, 256) + 512 * num_heads * 2 * (head_size + 4) * 4
+ *    (prefix sums of blocks per sequence, then two partial records per
+ *    workgroup and query head; fp32 KV needs none).
+ * Returns 0 for invalid sizes.  max_seq_len must be the value later passed to
+ * paged_attention_decode, or max_blocks_per_seq * block_size if 0 is passed.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
                                 int max_seq_len, int partition_size);
@@ -72,6 +85,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  * g = h / (num_heads / num_kv_heads) is row
  *   k_cache[block_tables[s, t / block_size], t % block_size, g, :]
  * (and likewise for v_cache).  seq_lens[s] == 0 gives a zero output row.
+ * Accumulation is fp32; for bf16/fp16 KV the softmax weights enter the
+ * weighted sum of V rounded to the KV type (the sum of weights stays fp32).
  *
  *  out            [num_seqs, num_heads, head_size], written (dtype)
  *  query          [num_seqs, num_heads, head_size] (dtype)
@@ -86,20 +101,25 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  *                 workspace); 0 means max_blocks_per_seq * block_size
  *  scale          softmax scale (usually 1/sqrt(head_size))
  *  dtype          pa_dtype of query, caches and out
- *  partition_size 0: one pass per (sequence, kv head).
+ *  partition_size 0: the library splits the work.  For bf16/fp16 the whole
+ *                 batch's blocks are cut into equal shares over the GPU
+ *                 (sequences that straddle a share are merged by a second
+ *                 kernel); needs a workspace; at most 16383 sequences.  For
+ *                 fp32 one pass per (sequence, kv head), no workspace.
  *                 > 0: split context into partitions of this many tokens (a
  *                 multiple of block_size); a second kernel merges partitions
- *                 with log-sum-exp weights.  Needs `workspace`.
+ *                 with log-sum-exp weights.  Needs a workspace.
+ *  flags          0 or PA_FLAG_SHARED_BLOCKS
  *  workspace      device buffer of >= pa_decode_workspace_size(...) bytes,
- *                 256-byte aligned, used only when partition_size > 0
- *                 (may be NULL otherwise).  Its contents are scratch.
+ *                 256-byte aligned, NULL when none is needed.  Its contents
+ *                 are scratch; calls that overlap in time need their own.
  */
 int paged_attention_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* seq_lens,
                            int num_seqs, int num_heads, int num_kv_heads, int head_size,
                            int block_size, int max_blocks_per_seq, int num_blocks,
                            int max_seq_len, float scale, int dtype, int partition_size,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Scatter new tokens' K/V rows into their cache slots (csdn article,

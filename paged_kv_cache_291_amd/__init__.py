@@ -10,7 +10,9 @@ from ._binding import (  # noqa: F401
     DTYPE_CODES,
     EXPORTED,
     LIB_PATH,
+    PA_FLAG_SHARED_BLOCKS,
     PagedAttnError,
+    decode_workspace_bytes,
     load_library,
     pa_decode_workspace_size,
     pa_status_string,

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_FLAG_SHARED_BLOCKS = 1
 DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache")
@@ -49,7 +50,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [c_int] * 5
     lib.paged_attention_decode.restype = c_int
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
-                                           c_int, c_int, c_int, c_float, c_int, c_int, vp, c_size, vp]
+                                           c_int, c_int, c_int, c_float, c_int, c_int, ctypes.c_uint, vp,
+                                           c_size, vp]
     lib.reshape_and_cache.restype = c_int
     lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
     if path is None:
@@ -90,16 +92,30 @@ def _stream(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def decode_workspace_bytes(query: torch.Tensor, block_tables: torch.Tensor, block_size: int,
+                           partition_size: int = 0, max_seq_len: int = 0) -> int:
+    """Workspace bytes a call with these arguments needs (0 if none)."""
+    S, Hq, D = query.shape
+    if partition_size == 0 and query.dtype == torch.float32:
+        return 0
+    msl = max_seq_len if max_seq_len > 0 else block_tables.shape[1] * block_size
+    return pa_decode_workspace_size(S, Hq, D, msl, partition_size)
+
+
 def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
                            v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                            scale: float, partition_size: int = 0, max_seq_len: int = 0,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                           workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                           stream=None) -> torch.Tensor:
     """Enqueue paged decode attention on ``stream`` (default: torch's current stream).
 
     Shapes: out/query ``[S, Hq, D]``; caches ``[NB, BS, Hkv, D]``;
     block_tables int32 ``[S, max_blocks]``; seq_lens int32 ``[S]``.
-    With ``partition_size > 0`` a workspace is needed: pass one (uint8 device
-    tensor, 256-byte aligned) or let this wrapper allocate it.
+    ``partition_size`` 0 lets the library balance the work, > 0 splits every
+    sequence into partitions of that many tokens.  When a workspace is needed
+    (see ``decode_workspace_bytes``) pass one (uint8 device tensor, 256-byte
+    aligned) or let this wrapper allocate it.  ``flags``:
+    ``PA_FLAG_SHARED_BLOCKS`` when blocks are shared between sequences.
     """
     S, Hq, D = query.shape
     NB, BS, Hkv, Dk = k_cache.shape
@@ -111,17 +127,16 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
     if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and seq_lens [S]")
     ws_ptr, ws_bytes = 0, 0
-    if partition_size > 0:
-        msl = max_seq_len if max_seq_len > 0 else block_tables.shape[1] * BS
-        need = pa_decode_workspace_size(S, Hq, D, msl, partition_size)
+    need = decode_workspace_bytes(query, block_tables, BS, partition_size, max_seq_len)
+    if need > 0:
         if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     rc = load_library().paged_attention_decode(
         _dev(out, "out", dt), _dev(query, "query", dt), _dev(k_cache, "k_cache", dt),
         _dev(v_cache, "v_cache", dt), _dev(block_tables, "block_tables", torch.int32),
         _dev(seq_lens, "seq_lens", torch.int32), S, Hq, Hkv, D, BS, block_tables.shape[1], NB,
-        int(max_seq_len), float(scale), DTYPE_CODES[dt], int(partition_size), ws_ptr, ws_bytes,
+        int(max_seq_len), float(scale), DTYPE_CODES[dt], int(partition_size), int(flags), ws_ptr, ws_bytes,
         _stream(stream))
     _check(rc)
     return out

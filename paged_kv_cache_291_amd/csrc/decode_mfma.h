@@ -1,0 +1,364 @@
+// Paged decode on the matrix cores (16-bit KV: bf16, fp16).
+//
+// One wave works on one (sequence, kv head) at a time; per 16-token block:
+//   QK:  S^T[t][h] = sum_d K[t][d] Q[h][d]: 16x16x32 MFMAs over head_size,
+//        tokens on M, the G query heads of the group on N (rows >= G zero).
+//        Lane l receives S[h = l%16][t = 4*(l/16) + i], i < 4.
+//   PV:  O[h][d] += sum_t P[h][t] V[t][d]: one 16x16x16 MFMA per 16-wide tile
+//        of head_size.  The score layout above is exactly the A operand
+//        (P[h = l%16][t = 4*(l/16) + j]).  V rows are loaded so that lane l
+//        holds rows t = 4*(l/16) + j, j < 4, and the elements
+//        d = VE*(l%16) .. VE*(l%16)+VE-1; output column n of tile T then maps
+//        to d = VE*n + T, so each B operand is element T of the lane's four
+//        rows (two byte permutes).  No LDS is used.
+//   Softmax: base 2 (scale * log2(e) applied to the score), probabilities
+//        rounded to the KV type for the PV product, sums in fp32.  Scores are
+//        only rescaled when a block maximum exceeds the running reference by
+//        more than 2^8; until then probabilities are taken against the stale
+//        reference, which is the same sum re-associated.
+//
+// Two launch shapes share this core:
+//  * pa_decode_mfma_kernel: one wave per (sequence, kv head, partition) -
+//    the split-context path with a fixed partition size.
+//  * pa_decode_sk_kernel: balanced split.  The (sequence, block) pairs of the
+//    whole batch are laid end to end and cut into equal ranges, one per
+//    workgroup; a workgroup has one wave per kv head of a head group, so a
+//    block's heads (one contiguous stretch of the pool) are read together.
+//    A sequence that crosses a range boundary leaves partial records that a
+//    merge kernel combines.
+#pragma once
+
+#include "common.h"
+
+namespace pa {
+
+// Rescale only when a score exceeds the reference by more than 2^8 (see above).
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D>
+struct MfmaShape {
+  static constexpr int kRow = D * 2;      // bytes of one token row of one head
+  static constexpr int kKs = D / 32;      // QK steps, 16 bytes of K per lane each
+  static constexpr int kVe = D / 16;      // V elements per lane per row = PV tiles
+  static constexpr int kVw = kVe / 2;     // ... as dwords
+  static_assert(D == 64 || D == 128, "head_size 64 or 128");
+};
+
+// Per-wave state of one (sequence, kv head) segment.
+template <int D>
+struct MfmaState {
+  u32x4 qb[MfmaShape<D>::kKs];   // Q^T operand: lane l holds Q[h = l%16][d = 32*step + 8*(l/16) ..]
+  float m_ref;                    // reference max of head l%16 (base-2 units)
+  float l_part;                   // this lane's share of the softmax sum of head l%16
+  f32x4 acc[MfmaShape<D>::kVe];   // O[h = 4*(l/16) + i][d = VE*(l%16) + T]
+};
+
+template <int D, int G>
+__device__ __forceinline__ void mfma_begin(MfmaState<D>& st, const void* query, int64_t q_row0, int g, int c) {
+  using SH = MfmaShape<D>;
+  const char* qrow = static_cast<const char*>(query) + (q_row0 + c) * SH::kRow + 16 * g;
+#pragma unroll
+  for (int k = 0; k < SH::kKs; ++k)
+    st.qb[k] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 64 * k) : u32x4{0u, 0u, 0u, 0u};
+  st.m_ref = -INFINITY;
+  st.l_part = 0.f;
+#pragma unroll
+  for (int T = 0; T < SH::kVe; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Blocks [b_begin, b_end) of one sequence for kv head `kvh`; tokens at or past
+// t_end are masked.  Returns true if a block id of the range is out of the
+// pool (the segment's result is then undefined and must be reported as NaN).
+template <class E, int D, bool NT>
+__device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __restrict__ k_cache,
+                                             const char* __restrict__ v_cache, const int* __restrict__ bt_row,
+                                             int b_begin, int b_end, int t_end, int num_blocks,
+                                             int num_kv_heads, int kvh, float qk_scale, int lane) {
+  using SH = MfmaShape<D>;
+  using M = Mfma<E>;
+  constexpr int BS = kBlockSize, KS = SH::kKs, VE = SH::kVe, VW = SH::kVw;
+  const int g = lane >> 4, c = lane & 15;
+  const int blk_bytes = BS * num_kv_heads * SH::kRow;
+  const int row_stride = num_kv_heads * SH::kRow;
+  const int k_off = (c * num_kv_heads + kvh) * SH::kRow + 16 * g;             // K row t = l%16
+  const int v_off = (4 * g * num_kv_heads + kvh) * SH::kRow + VE * 2 * c;     // V row t = 4*(l/16) + j
+
+  struct Blk {
+    u32x4 k[KS];
+    uint32_t v[4][VW];
+  };
+
+  auto load_block = [&](int phys, Blk& b) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(k_cache + (int64_t)phys * blk_bytes, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(v_cache + (int64_t)phys * blk_bytes, blk_bytes);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) b.k[k] = load16<NT>(rk, k_off, 64 * k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (VW == 4) {
+        const u32x4 t = load16<NT>(rv, v_off, j * row_stride);
+        b.v[j][0] = t[0]; b.v[j][1] = t[1]; b.v[j][2] = t[2]; b.v[j][3] = t[3];
+      } else {
+        const u32x2 t = load8<NT>(rv, v_off, j * row_stride);
+        b.v[j][0] = t[0]; b.v[j][1] = t[1];
+      }
+    }
+  };
+
+  auto consume = [&](const Blk& b, int valid, bool masked) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) sc = M::qk(b.k[k], st.qb[k], sc);
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = sc[i] * qk_scale;
+      if (masked && 4 * g + i >= valid) z[i] = -INFINITY;
+    }
+    const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
+      const float m_new = fmaxf(st.m_ref, bm);
+      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first block
+      st.l_part *= alpha;
+      float ar[4];                                                     // factors of rows h = 4*(l/16) + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int T = 0; T < VE; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[T][i] *= ar[i];
+      st.m_ref = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - st.m_ref);
+    st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
+    const u32x2 pa = {pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
+
+    uint32_t v[4][VW];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < VW; ++q) v[j][q] = (masked && 4 * g + j >= valid) ? 0u : b.v[j][q];
+#pragma unroll
+    for (int T = 0; T < VE; ++T) {
+      const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;   // high or low half of each dword
+      const u32x2 vb = {__builtin_amdgcn_perm(v[1][T >> 1], v[0][T >> 1], sel),
+                        __builtin_amdgcn_perm(v[3][T >> 1], v[2][T >> 1], sel)};
+      st.acc[T] = M::pv(pa, vb, st.acc[T]);
+    }
+  };
+
+  // Block ids: up to 64 per batch, one per lane, then broadcast with readlane.
+  // Two register sets alternate so the next block's loads are in flight while
+  // the current block is consumed; inside the steady-state loop every load is
+  // unconditional, which lets each consume wait only for its own block.  Only
+  // the segment's last block can be partial.
+  const int last_valid = t_end - (b_end - 1) * BS;
+  for (int cb = b_begin; cb < b_end; cb += 64) {
+    const int n = min(64, b_end - cb);
+    const int id = lane < n ? bt_row[cb + lane] : 0;
+    if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) return true;
+    const bool last_batch = cb + 64 >= b_end;
+    Blk A, B;
+    load_block(__builtin_amdgcn_readlane(id, 0), A);
+    int j = 0;
+    for (; j + 2 < n; j += 2) {
+      load_block(__builtin_amdgcn_readlane(id, j + 1), B);
+      consume(A, BS, false);
+      load_block(__builtin_amdgcn_readlane(id, j + 2), A);
+      consume(B, BS, false);
+    }
+    const int vj = (last_batch && j == n - 1) ? last_valid : BS;
+    if (j + 1 < n) {
+      load_block(__builtin_amdgcn_readlane(id, j + 1), B);
+      consume(A, BS, false);
+      const int vj1 = last_batch ? last_valid : BS;
+      if (vj1 >= BS) consume(B, BS, false);
+      else consume(B, vj1, true);
+    } else if (vj >= BS) {
+      consume(A, BS, false);
+    } else {
+      consume(A, vj, true);
+    }
+  }
+  return false;
+}
+
+// Normalise and write the G heads of the segment: to `out` rows
+// out_row0 + h (rec == nullptr), or as partial records rec + h * rec_stride.
+template <class E, int D, int G>
+__device__ __forceinline__ void mfma_finish(const MfmaState<D>& st, bool bad, void* __restrict__ out,
+                                            int64_t out_row0, float* __restrict__ rec, int64_t rec_stride,
+                                            int lane) {
+  constexpr int VE = MfmaShape<D>::kVe;
+  const int g = lane >> 4, c = lane & 15;
+  const float l_head = rows_sum(st.l_part);                 // softmax sum of head l%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;                                  // this lane's output row
+    const float lh = __shfl(l_head, h);
+    const float mh = __shfl(st.m_ref, h);
+    if (h >= G) continue;
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    float o[VE];
+#pragma unroll
+    for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
+    if (rec == nullptr) {
+      store_run<E, VE>(out, (out_row0 + h) * D + VE * c, o);
+    } else {
+      float* r = rec + h * rec_stride;
+      store_f32_run<VE>(r + kRecHead + VE * c, o);
+      if (c == 0) {
+        r[0] = bad ? qnan() : mh;
+        r[1] = bad ? qnan() : lh;
+      }
+    }
+  }
+}
+
+// ---- split-context path: one wave per (sequence, kv head, partition)
+// ws: partial records [num_seqs * num_heads * num_parts].
+template <class E, int D, int G, bool NT>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
+                      const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+                      const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
+                      int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
+                      float qk_scale, int part_tokens, int num_parts, float* __restrict__ ws) {
+  constexpr int BS = kBlockSize;
+  constexpr int REC = rec_floats<D>();
+  const int lane = threadIdx.x;
+
+  int w = blockIdx.x;
+  const int kvh = w % num_kv_heads;
+  w /= num_kv_heads;
+  const int part = w % num_parts;
+  const int s = w / num_parts;
+  const int64_t row0 = (int64_t)s * num_heads + kvh * G;
+
+  MfmaState<D> st;
+  mfma_begin<D, G>(st, query, row0, lane >> 4, lane & 15);
+
+  const int L = seq_lens[s];
+  const int64_t cap = min((int64_t)max_blocks * BS, (int64_t)num_parts * part_tokens);
+  const bool bad_len = L < 0 || (int64_t)L > cap;
+  const int nparts_seq = bad_len ? 1 : ceil_div(L, part_tokens);
+  if (part >= (nparts_seq > 0 ? nparts_seq : 1)) return;      // empty partition
+  const bool final_write = nparts_seq <= 1;
+
+  const int t_begin = part * part_tokens;
+  const int t_end = bad_len ? 0 : min(L, t_begin + part_tokens);
+  bool bad = bad_len;
+  if (!bad_len && t_end > t_begin)
+    bad = mfma_segment<E, D, NT>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+                                 t_begin / BS, ceil_div(t_end, BS), t_end, num_blocks, num_kv_heads, kvh,
+                                 qk_scale, lane);
+  mfma_finish<E, D, G>(st, bad, out, row0, final_write ? nullptr : ws + (row0 * num_parts + part) * REC,
+                       (int64_t)num_parts * REC, lane);
+}
+
+// ---- balanced split (stream-K over the batch's blocks)
+
+// Range of flattened blocks of workgroup `rank` (of nwg) when U blocks are
+// split evenly: [rank*U/nwg, (rank+1)*U/nwg).
+__host__ __device__ inline int sk_range_begin(int rank, int U, int nwg) {
+  return (int)(((int64_t)rank * U) / nwg);
+}
+
+// Workgroup whose range holds flattened block u (u < U).
+__host__ __device__ inline int sk_owner(int u, int U, int nwg) {
+  return (int)((((int64_t)u + 1) * nwg - 1) / U);
+}
+
+// Exclusive prefix sums of the blocks per sequence into s_cum[0..num_seqs];
+// sequences with an out-of-contract length count zero blocks.
+__device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int num_seqs, int max_blocks,
+                                         int* s_cum, int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  int carry = 0;
+  for (int base = 0; base < num_seqs; base += blockDim.x) {
+    const int s = base + tid;
+    int x = 0;
+    if (s < num_seqs) {
+      const int L = seq_lens[s];
+      x = (L > 0 && (int64_t)L <= (int64_t)max_blocks * kBlockSize) ? ceil_div(L, kBlockSize) : 0;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w2 = 0; w2 < nwaves; ++w2) {
+      const int t = s_wsum[w2];
+      before += w2 < wave ? t : 0;
+      total += t;
+    }
+    if (s < num_seqs) s_cum[s + 1] = carry + before + x;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) s_cum[0] = 0;
+  __syncthreads();
+}
+
+// Grid: head_groups * nwg workgroups of hpw waves (kv heads hg*hpw + wave).
+// Dynamic LDS: (num_seqs + 1) ints.  ws_cum: num_seqs + 1 ints (written by
+// workgroup 0 for the merge kernel); ws_rec: partial records, 2 slots per
+// workgroup (first and last segment of its range) * hpw * G heads.
+// A workgroup is up to 8 waves; 12 wave slots per CU would still hold only
+// one, so the register budget is that of 2 waves per SIMD.
+template <class E, int D, int G, bool NT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
+                    const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+                    const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
+                    int num_seqs, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
+                    float qk_scale, int hpw, int nwg, int* __restrict__ ws_cum, float* __restrict__ ws_rec) {
+  constexpr int BS = kBlockSize;
+  constexpr int REC = rec_floats<D>();
+  extern __shared__ int s_cum[];
+  __shared__ int s_wsum[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = blockIdx.x / nwg, rank = blockIdx.x - hg * nwg;
+  const int kvh = hg * hpw + wave;
+
+  blocks_prefix_sum(seq_lens, num_seqs, max_blocks, s_cum, s_wsum);
+  const int U = s_cum[num_seqs];
+  if (blockIdx.x == 0)
+    for (int i = tid; i <= num_seqs; i += blockDim.x) ws_cum[i] = s_cum[i];
+  if (U == 0) return;
+  const int u0 = sk_range_begin(rank, U, nwg), u1 = sk_range_begin(rank + 1, U, nwg);
+  if (u0 >= u1) return;
+
+  // first sequence: the last s with s_cum[s] <= u0 (then s_cum[s + 1] > u0)
+  int lo = 0, hi = num_seqs;                 // invariant: s_cum[lo] <= u0 < s_cum[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_cum[mid] <= u0) lo = mid; else hi = mid;
+  }
+  int s = lo;
+  float* rec_wg = ws_rec + ((int64_t)blockIdx.x * 2 * hpw + wave) * G * REC;
+  for (int u = u0; u < u1;) {
+    const int c0 = s_cum[s], c1 = s_cum[s + 1];
+    if (c1 == c0) { ++s; continue; }
+    const int b0 = u - c0, b1 = min(c1, u1) - c0;
+    const int L = seq_lens[s];
+    const int64_t row0 = (int64_t)s * num_heads + kvh * G;
+    MfmaState<D> st;
+    mfma_begin<D, G>(st, query, row0, lane >> 4, lane & 15);
+    const bool bad = mfma_segment<E, D, NT>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, b0, b1,
+                                            min(L, b1 * BS), num_blocks, num_kv_heads, kvh, qk_scale, lane);
+    const bool whole = b0 == 0 && b1 == c1 - c0;
+    float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * G * REC);
+    mfma_finish<E, D, G>(st, bad, out, row0, rec, REC, lane);
+    u += b1 - b0;
+    ++s;
+  }
+}
+
+}  // namespace pa

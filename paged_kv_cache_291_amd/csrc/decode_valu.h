@@ -1,0 +1,266 @@
+// Paged decode on the vector ALUs (used for fp32 KV).
+//
+// One 64-lane wave (one workgroup) per work item (sequence, kv head, chunk of
+// tokens; with part_tokens == 0 the chunk is the whole sequence):
+//  * Gather loader: the item's block ids are read one per lane and broadcast
+//    with readlane.  One row of one head (head_size * elem bytes) is read by
+//    LPR lanes with 16-byte buffer loads, so one load instruction covers
+//    64/LPR token rows and a block is NI = 16 / (64/LPR) instructions per
+//    cache.  Two register sets alternate so the next block is in flight while
+//    the current one is consumed.
+//  * Scores: q stays in registers; each lane forms partial dots of its
+//    16-byte slice for all G query heads of the group, so each K byte is read
+//    once per kv head.  A halving butterfly over the LPR lanes (DPP row/half
+//    mirror and quad permutes) leaves every score on one lane.
+//  * Online softmax (base 2, scale * log2(e) applied to the score) per
+//    "sub-wave" (the LPR lanes that share token rows); probabilities and
+//    rescale factors go through a small LDS buffer of the wave so every lane
+//    can weight its V slice; PV accumulates in fp32 registers.
+//  * At the end the sub-waves are merged with log-sum-exp weights.
+//  * Masking uses selects only (the pool may hold NaN in dead slots).
+#pragma once
+
+#include "common.h"
+
+namespace pa {
+
+template <class E, int D, int G>
+struct ValuCfg {
+  static constexpr int kRow = D * E::kBytes;        // bytes of one token row of one head
+  static constexpr int kLpr = kRow / 16;            // lanes per row
+  static constexpr int kRpi = 64 / kLpr;            // rows per load instruction
+  static constexpr int kNi = kBlockSize / kRpi;     // load instructions per block
+  static constexpr int kEpl = 16 / E::kBytes;       // elements per lane per instruction
+  static constexpr int kNv = kNi * G;               // partial scores per lane per block
+  static constexpr int kNvl = kNv > kLpr ? kNv / kLpr : 1;
+  static constexpr int kNh = ilog2(kNv < kLpr ? kNv : kLpr);
+  static constexpr int kPStride = round_up4(kNv + G);
+  static_assert(kLpr >= 4 && kLpr <= 32, "row must span 4..32 lanes");
+  static_assert(kBlockSize % kRpi == 0 && kNi == kLpr / 4, "block must be whole load instructions");
+  static_assert(D % 64 == 0, "head_size must be a multiple of 64");
+};
+
+template <class E, int D, int G>
+struct ValuOccupancy {
+  // 3 waves per SIMD need <= 168 VGPRs, which head_size 64 meets up to G = 4
+  static constexpr int kWaves = (G <= 4 && (E::kBytes == 2 || D == 64)) ? 3 : 1;
+};
+
+// ws: partial records [num_seqs * num_heads * num_parts] (split mode only).
+template <class E, int D, int G>
+__global__ void __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(ValuOccupancy<E, D, G>::kWaves, 8)))
+pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
+                      const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+                      const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
+                      int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
+                      float qk_scale, int part_tokens, int num_parts, float* __restrict__ ws) {
+  using C = ValuCfg<E, D, G>;
+  constexpr int BS = kBlockSize;
+  constexpr int LPR = C::kLpr, RPI = C::kRpi, NI = C::kNi, EPL = C::kEpl;
+  constexpr int NV = C::kNv, NVL = C::kNvl, NH = C::kNh;
+  constexpr int REC = rec_floats<D>();
+
+  __shared__ __align__(16) float s_p[RPI][C::kPStride];
+  __shared__ float s_m[RPI][G];
+  __shared__ float s_l[RPI][G];
+
+  const int lane = threadIdx.x;
+  const int r = lane / LPR, c = lane % LPR;
+
+  // Work item; the kv head varies fastest.
+  int w = blockIdx.x;
+  const int kvh = w % num_kv_heads;
+  w /= num_kv_heads;
+  const int part = w % num_parts;
+  const int s = w / num_parts;
+  const int hq0 = kvh * G;                                      // first query head of the group
+
+  u32x4 qv[G];
+  {
+    const char* qb = static_cast<const char*>(query) + ((int64_t)s * num_heads + hq0) * C::kRow + c * 16;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(qb + h * C::kRow);
+  }
+
+  const int L = seq_lens[s];
+  const bool split = part_tokens > 0;
+  // tokens this launch can cover: the table row, and in split mode the grid's partitions
+  const int64_t cap = split ? min((int64_t)max_blocks * BS, (int64_t)num_parts * part_tokens)
+                            : (int64_t)max_blocks * BS;
+  const bool bad_len = L < 0 || (int64_t)L > cap;
+  const int nparts_seq = bad_len ? 1 : (split ? ceil_div(L, part_tokens) : 1);
+  if (part >= (nparts_seq > 0 ? nparts_seq : 1)) return;      // empty partition
+  const bool final_write = !split || nparts_seq <= 1;          // this item writes `out`
+
+  const int t_begin = split ? part * part_tokens : 0;
+  const int t_end = bad_len ? 0 : (split ? min(L, t_begin + part_tokens) : L);
+  const int b_begin = t_begin / BS;
+  const int b_end = ceil_div(t_end, BS);
+
+  const int blk_bytes = BS * num_kv_heads * C::kRow;
+  const int row_stride = num_kv_heads * C::kRow;                // bytes between token rows
+  const int lane_off = (r * num_kv_heads + kvh) * C::kRow + c * 16;
+
+  float m_run[NVL], l_run[NVL];
+  float acc[G][EPL];
+#pragma unroll
+  for (int k = 0; k < NVL; ++k) { m_run[k] = -INFINITY; l_run[k] = 0.f; }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+
+  const int idx0 = (c >> (ilog2(LPR) - NH)) * NVL;             // first score index this lane owns
+  float* pbuf = &s_p[r][0];
+
+  auto load_block = [&](int phys, u32x4* kb, u32x4* vb) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(k_cache + (int64_t)phys * blk_bytes, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(v_cache + (int64_t)phys * blk_bytes, blk_bytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kb[i] = load16<true>(rk, lane_off, i * RPI * row_stride);
+      vb[i] = load16<true>(rv, lane_off, i * RPI * row_stride);
+    }
+  };
+
+  auto consume = [&](const u32x4* kb, const u32x4* vb, int valid, bool masked) {
+    float sc[NV];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[i * G + h] = dot16<E>(qv[h], kb[i], 0.f);
+    transpose_reduce<LPR, NV, ilog2(LPR) - 1>(sc, c);
+
+    float p[NVL], alpha[NVL];
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+      const int i = (idx0 + k) / G;
+      float z = sc[k] * qk_scale;
+      if (masked && i * RPI + r >= valid) z = -INFINITY;
+      const float bm = igroup_max<LPR>(z);
+      const float m_new = fmaxf(m_run[k], bm);
+      // a sub-wave may not have seen a valid token yet: keep exp2 away from -inf - -inf
+      const float m_use = (masked && m_new == -INFINITY) ? 0.f : m_new;
+      alpha[k] = __builtin_amdgcn_exp2f(m_run[k] - m_use);
+      p[k] = __builtin_amdgcn_exp2f(z - m_use);
+      l_run[k] = fmaf(l_run[k], alpha[k], p[k]);
+      m_run[k] = m_new;
+    }
+#pragma unroll
+    for (int k = 0; k < NVL; ++k) {
+      pbuf[idx0 + k] = p[k];
+      if (idx0 + k < G) pbuf[NV + idx0 + k] = alpha[k];
+    }
+    wave_lds_sync();
+    float pall[C::kPStride];
+#pragma unroll
+    for (int j = 0; j < C::kPStride; j += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(pbuf + j);
+      pall[j] = t.x; pall[j + 1] = t.y; pall[j + 2] = t.z; pall[j + 3] = t.w;
+    }
+    wave_lds_sync();
+
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= pall[NV + h];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      u32x4 v = vb[i];
+      if (masked && i * RPI + r >= valid) v = u32x4{0u, 0u, 0u, 0u};
+      float vf[EPL];
+      widen16<E>(v, vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ph = pall[i * G + h];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+      }
+    }
+  };
+
+  const int* bt = block_tables + (int64_t)s * max_blocks;
+  bool bad = bad_len;
+  for (int cb = b_begin; cb < b_end; cb += 64) {
+    const int n = min(64, b_end - cb);
+    const int id = lane < n ? bt[cb + lane] : 0;
+    if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) { bad = true; break; }
+    const bool last_batch = cb + 64 >= b_end;
+    const int last_valid = t_end - (b_end - 1) * BS;
+    u32x4 ka[NI], va[NI], kb2[NI], vb2[NI];
+    load_block(__builtin_amdgcn_readlane(id, 0), ka, va);
+    int j = 0;
+    for (; j + 2 < n; j += 2) {                                 // blocks j, j+1 full; j+2 exists
+      load_block(__builtin_amdgcn_readlane(id, j + 1), kb2, vb2);
+      consume(ka, va, BS, false);
+      load_block(__builtin_amdgcn_readlane(id, j + 2), ka, va);
+      consume(kb2, vb2, BS, false);
+    }
+    const int vj = (last_batch && j == n - 1) ? last_valid : BS;
+    if (j + 1 < n) {
+      load_block(__builtin_amdgcn_readlane(id, j + 1), kb2, vb2);
+      consume(ka, va, BS, false);
+      const int vj1 = last_batch ? last_valid : BS;
+      if (vj1 >= BS) consume(kb2, vb2, BS, false);
+      else consume(kb2, vb2, vj1, true);
+    } else if (vj >= BS) {
+      consume(ka, va, BS, false);
+    } else {
+      consume(ka, va, vj, true);
+    }
+  }
+
+  // ---- merge the sub-waves (token rows r) with log-sum-exp weights
+#pragma unroll
+  for (int k = 0; k < NVL; ++k) {
+    l_run[k] = igroup_sum<LPR>(l_run[k]);
+    if (idx0 + k < G) {
+      s_m[r][idx0 + k] = m_run[k];
+      s_l[r][idx0 + k] = l_run[k];
+    }
+  }
+  wave_lds_sync();
+  float Mh[G], Lh[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int r2 = 0; r2 < RPI; ++r2) M = fmaxf(M, s_m[r2][h]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    float Ls = 0.f;
+#pragma unroll
+    for (int r2 = 0; r2 < RPI; ++r2) Ls += s_l[r2][h] * __builtin_amdgcn_exp2f(s_m[r2][h] - Ms);
+    const float f = __builtin_amdgcn_exp2f(s_m[r][h] - Ms);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float a = acc[h][e] * f;
+#pragma unroll
+      for (int m = LPR; m < 64; m <<= 1) a += __shfl_xor(a, m);
+      acc[h][e] = a;
+    }
+    Mh[h] = M;
+    Lh[h] = Ls;
+  }
+  if (r != 0) return;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float inv = Lh[h] > 0.f ? 1.f / Lh[h] : 0.f;
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = bad ? qnan() : acc[h][e] * inv;
+    const int64_t sh = (int64_t)s * num_heads + hq0 + h;
+    if (final_write) {
+      store_run<E, EPL>(out, sh * D + c * EPL, o);
+    } else {
+      float* rec = ws + (sh * num_parts + part) * REC;
+      store_f32_run<EPL>(rec + kRecHead + c * EPL, o);
+      if (c == 0) {
+        rec[0] = bad ? qnan() : Mh[h];
+        rec[1] = bad ? qnan() : Lh[h];
+      }
+    }
+  }
+}
+
+}  // namespace pa

@@ -26,7 +26,7 @@ def to_device(wl: W.Workload, dev="cuda"):
     return d
 
 
-def gpu_decode(wl: W.Workload, dev_inputs=None, partition_size=None, scatter=True):
+def gpu_decode(wl: W.Workload, dev_inputs=None, partition_size=None, scatter=True, flags=0):
     """Scatter (if the workload has new tokens) then decode on the GPU."""
     import paged_kv_cache_291_amd as P
     d = dev_inputs or to_device(wl)
@@ -35,7 +35,7 @@ def gpu_decode(wl: W.Workload, dev_inputs=None, partition_size=None, scatter=Tru
     out = torch.empty_like(d["q"])
     ps = wl.partition_size if partition_size is None else partition_size
     P.paged_attention_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
-                             partition_size=ps, max_seq_len=wl.max_seq_len)
+                             partition_size=ps, max_seq_len=wl.max_seq_len, flags=flags)
     torch.cuda.synchronize()
     return out.cpu(), d
 

@@ -14,14 +14,17 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_cache_291_amd as P
 from paged_kv_cache_291_amd import workloads as W
 
 from helpers import HALF_ULP, TOL, errors, gpu_decode, oracle_decode, sample_seqs, to_device
 
 pytestmark = pytest.mark.gpu
 
-# partition sizes each workload is run with: single pass and the split path
-CONFIG_PARTITIONS = {1: (0, 16), 2: (0, 512), 3: (0, 512), 4: (512, 0), 5: (0, 512)}
+# partition sizes each workload is run with: 0 (the library's own split) and a fixed split
+CONFIG_PARTITIONS = {1: (0, 16), 2: (0, 512), 3: (0, 512), 4: (0, 512), 5: (0, 512)}
+# workloads whose blocks are shared between sequences also run with the cacheable-load flag
+CONFIG_FLAGS = {5: P.PA_FLAG_SHARED_BLOCKS}
 SAMPLE = {1: 4, 2: 6, 3: 12, 4: 8, 5: 8}
 
 
@@ -34,17 +37,21 @@ def test_config_parity(cfg, seed):
     ref = oracle_decode(wl, seqs)
     dev = to_device(wl)
     if wl.slot_mapping is not None:
-        import paged_kv_cache_291_amd as P
         P.reshape_and_cache(dev["nk"], dev["nv"], dev["kc"], dev["vc"], dev["sm"])
     outs = {}
-    for ps in CONFIG_PARTITIONS[cfg]:
-        out, _ = gpu_decode(wl, dev, partition_size=ps, scatter=False)
-        assert torch.isfinite(out.float()).all(), f"non-finite output (partition {ps})"
+    runs = [(ps, 0) for ps in CONFIG_PARTITIONS[cfg]]
+    if cfg in CONFIG_FLAGS:
+        runs += [(ps, CONFIG_FLAGS[cfg]) for ps in CONFIG_PARTITIONS[cfg]]
+    for ps, flags in runs:
+        out, _ = gpu_decode(wl, dev, partition_size=ps, scatter=False, flags=flags)
+        assert torch.isfinite(out.float()).all(), f"non-finite output (partition {ps}, flags {flags})"
         err, _, _ = errors(out[seqs], ref)
-        print(f"  partition={ps}: max-abs err {err:.3e} (tol {TOL[wl.dtype]})", flush=True)
+        print(f"  partition={ps} flags={flags}: max-abs err {err:.3e} (tol {TOL[wl.dtype]})", flush=True)
         assert err <= TOL[wl.dtype]
-        outs[ps] = out
-    a, b = outs.values()
+        if flags:
+            assert torch.equal(out, outs[(ps, 0)])          # the cache policy changes no arithmetic
+        outs[(ps, flags)] = out
+    a, b = outs[runs[0]], outs[runs[1]]
     tol = 2 * TOL[wl.dtype]
     assert (a.float() - b.float()).abs().max().item() <= tol
 
@@ -102,9 +109,54 @@ def test_cow_shared_prefix_bit_identical():
         assert torch.equal(a, b)
 
 
-def test_repeat_runs_bit_identical():
+@pytest.mark.parametrize("ps", [0, 512])
+def test_repeat_runs_bit_identical(ps):
     wl = W.make_config(3, 0, poison=True)
     dev = to_device(wl)
-    a, _ = gpu_decode(wl, dev, partition_size=512)
-    b, _ = gpu_decode(wl, dev, partition_size=512)
+    a, _ = gpu_decode(wl, dev, partition_size=ps)
+    b, _ = gpu_decode(wl, dev, partition_size=ps)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 32, 8), ("f16", 12, 12), ("bf16", 8, 2), ("bf16", 16, 16)])
+def test_many_short_sequences(dtype, Hq, Hkv):
+    """Hundreds of short sequences (many per workgroup range, empty ones
+    between them, more sequences than threads in the prefix-sum pass)."""
+    rng = np.random.default_rng(Hq * 100 + Hkv)
+    lens = rng.integers(0, 70, size=700)
+    lens[::37] = 0
+    lens[5] = 2000                                         # one long sequence spanning several ranges
+    wl = W.make_random(Hq + Hkv, len(lens), Hq, Hkv, 128, dtype, lens)
+    ref = oracle_decode(wl)
+    for ps, flags in ((0, 0), (0, P.PA_FLAG_SHARED_BLOCKS), (32, 0)):
+        out, _ = gpu_decode(wl, partition_size=ps, flags=flags)
+        _, g, diff = errors(out, ref)
+        bound = TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)
+        assert np.isfinite(g).all()
+        assert float(np.max(diff - bound)) <= 0.0, (ps, flags, float(diff.max()))
+        assert (g[lens == 0] == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ps", [0, 16])
+def test_contract_violations_give_nan_rows(dtype, ps):
+    """Out-of-contract lengths and block ids never fault: those rows are NaN,
+    every other row is still right."""
+    lens = [40, 33, 17, 50, 64, 20]
+    wl = W.make_random(31, len(lens), 8, 2, 64, dtype, lens, pool_factor=2.0, extra_table_cols=1)
+    bt = wl.block_tables.copy()
+    sl = wl.seq_lens.copy()
+    mb = bt.shape[1]
+    sl[1] = mb * 16 + 1                                    # longer than the table row
+    sl[2] = -5                                             # negative length
+    bt[3, 1] = wl.num_blocks                               # first id past the pool
+    bt[4, 2] = -1                                          # negative id inside the valid range
+    bad = [1, 2, 3, 4]
+    good = [0, 5]
+    wl2 = W.Workload(**{**wl.__dict__, "block_tables": bt, "seq_lens": sl})
+    out, _ = gpu_decode(wl2, partition_size=ps)
+    g = out.double().numpy()
+    for s in bad:
+        assert np.isnan(g[s]).all(), s
+    ref = oracle_decode(wl, seqs=good)
+    assert np.max(np.abs(g[good] - ref)) <= TOL[dtype] + HALF_ULP[dtype] * np.max(np.abs(ref))

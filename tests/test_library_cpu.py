@@ -42,20 +42,23 @@ def test_status_strings():
 
 
 def test_workspace_size_formula():
-    # num_seqs * num_heads * ceil(max_seq_len / partition) * (head_size + 2) * 4, ml part padded to 256
-    assert P.pa_decode_workspace_size(8, 64, 128, 32768, 512) == 8 * 64 * 64 * 2 * 4 + 8 * 64 * 64 * 128 * 4
-    assert P.pa_decode_workspace_size(3, 5, 64, 100, 16) == ((3 * 5 * 7 * 8 + 255) // 256) * 256 + 3 * 5 * 7 * 64 * 4
-    assert P.pa_decode_workspace_size(8, 64, 128, 32768, 0) == 0
+    # fixed partitions: one record of head_size + 4 floats per (sequence, head, partition)
+    assert P.pa_decode_workspace_size(8, 64, 128, 32768, 512) == 8 * 64 * 64 * 132 * 4
+    assert P.pa_decode_workspace_size(3, 5, 64, 100, 16) == 3 * 5 * 7 * 68 * 4
+    # balanced split: prefix sums (padded to 256 bytes) + 2 records per workgroup (512) and head
+    assert P.pa_decode_workspace_size(256, 32, 128, 4096, 0) == 1280 + 512 * 32 * 2 * 132 * 4
+    assert P.pa_decode_workspace_size(1, 8, 64, 0, 0) == 256 + 512 * 8 * 2 * 68 * 4
     assert P.pa_decode_workspace_size(-1, 64, 128, 32768, 512) == 0
+    assert P.pa_decode_workspace_size(8, 64, 128, 32768, -16) == 0
 
 
 def _decode(lib, **kw):
     a = dict(out=None, q=None, kc=None, vc=None, bt=None, sl=None, S=4, Hq=8, Hkv=8, D=64, BS=16,
-             MB=4, NB=64, msl=0, scale=0.125, dtype=0, ps=0, ws=None, wsb=0, stream=None)
+             MB=4, NB=64, msl=0, scale=0.125, dtype=0, ps=0, flags=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.paged_attention_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["S"], a["Hq"],
                                       a["Hkv"], a["D"], a["BS"], a["MB"], a["NB"], a["msl"], a["scale"],
-                                      a["dtype"], a["ps"], a["ws"], a["wsb"], a["stream"])
+                                      a["dtype"], a["ps"], a["flags"], a["ws"], a["wsb"], a["stream"])
 
 
 FAKE = 0x1000  # a non-null, aligned address that is never dereferenced on the host
@@ -77,6 +80,10 @@ def test_decode_host_errors():
     assert _decode(lib, ps=512, ws=FAKE, wsb=16, **ptrs) == -3   # too small
     assert _decode(lib, ps=16, ws=FAKE + 16, wsb=1 << 30, **ptrs) == -3   # misaligned workspace
     assert _decode(lib, S=-1, **ptrs) == -1
+    assert _decode(lib, flags=2, **ptrs) == -1                   # unknown flag
+    assert _decode(lib, dtype=2, **ptrs) == -3                   # bf16 balanced split needs a workspace
+    assert _decode(lib, dtype=1, ws=FAKE, wsb=16, **ptrs) == -3
+    assert _decode(lib, dtype=2, S=16384, ws=FAKE, wsb=1 << 40, **ptrs) == -2   # too many sequences
     p2 = dict(ptrs, q=FAKE + 2)
     assert _decode(lib, **p2) == -1                              # misaligned query
 
