@@ -33,7 +33,8 @@ METRIC = "paged decode attention: KV GB/s and % of HBM peak; us per decode step"
 DEFAULT_PARTITION = {1: 0, 2: 0, 3: 0, 4: 0, 5: 0}
 # the shared-prefix workload names the same blocks from many sequences
 DEFAULT_FLAGS = {5: 1}
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_291_amd", "csrc", "pagedattn.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "paged_kv_cache_291_amd", "csrc")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse():
@@ -49,26 +50,96 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--traffic-from", default="", metavar="FETCH_DIR,WRITE_DIR",
+                    help="no GPU run: turn two rocprofv3 --pmc result folders of this benchmark into "
+                         "profiles/traffic.json (pass the same --config/--partition/--copy-calibration)")
     return ap.parse_args()
 
 
 def source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of every kernel source file: counter results are tied to it."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        h.update(name.encode())
+        h.update(open(os.path.join(KERNEL_SRC_DIR, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel_name: str, workload: str):
-    """HBM bytes per launch from committed counter runs, if they were taken on
-    the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    """HBM bytes per decode step from committed counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        rec = json.load(open(path)).get(f"{kernel_name}|{workload}")
+        rec = json.load(open(TRAFFIC_JSON)).get(f"{kernel_name}|{workload}")
     except (OSError, ValueError):
         return None
     if not rec or rec.get("source_hash") != source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def traffic_from_counters(fetch_dir: str, write_dir: str, cfg: int, partition: int, flags: int):
+    """Turn two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
+    WRITE_SIZE, each with --copy-calibration) into HBM bytes per decode step.
+
+    Each counter is scaled by what it reads for the calibration copy (the last
+    plain copy dispatch, of known size): the ratio of known bytes to counted
+    bytes.  The result is stored in profiles/traffic.json under the step's
+    kernel names and the workload, with the hash of the kernel sources.
+    """
+    import csv
+    import glob
+
+    def rows(d, counter):
+        f = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        return [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+
+    out = {}
+    known = None
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rs = rows(d, counter)
+        copies = [r for r in rs if "copyBuffer" in r["Kernel_Name"]]
+        calib_kib = float(copies[-1]["Counter_Value"])
+        step = {}
+        for r in rs:
+            name = r["Kernel_Name"]
+            if "pa::" not in name or "scatter" in name:
+                continue
+            short = name.split("<")[0].split("::")[-1]
+            step.setdefault(short, []).append(float(r["Counter_Value"]))
+        out[counter] = (calib_kib, {k: sum(v) / len(v) for k, v in step.items()})
+    return out
+
+
+def write_traffic(args):
+    fetch_dir, write_dir = args.traffic_from.split(",")
+    cfg = args.config
+    ps = DEFAULT_PARTITION[cfg] if args.partition < 0 else args.partition
+    flags = DEFAULT_FLAGS.get(cfg, 0) if args.flags < 0 else args.flags
+    res = traffic_from_counters(fetch_dir, write_dir, cfg, ps, flags)
+    calib_bytes = args.copy_calibration << 20
+    f_calib, f_kern = res["FETCH_SIZE"]
+    w_calib, w_kern = res["WRITE_SIZE"]
+    f_scale = calib_bytes / (f_calib * 1024.0)
+    w_scale = calib_bytes / (w_calib * 1024.0)
+    names = sorted(f_kern, key=lambda k: -f_kern[k])
+    fetch = sum(f_kern[k] for k in names) * 1024.0 * f_scale
+    write = sum(w_kern.get(k, 0.0) for k in names) * 1024.0 * w_scale
+    key = "+".join(names) + f"|cfg{cfg}"
+    db = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    db[key] = {
+        "source_hash": source_hash(),
+        "bytes_per_launch": int(round(fetch + write)),
+        "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "per_kernel_fetch_bytes": {k: int(round(f_kern[k] * 1024.0 * f_scale)) for k in names},
+        "per_kernel_write_bytes": {k: int(round(w_kern.get(k, 0.0) * 1024.0 * w_scale)) for k in names},
+        "partition_size": ps, "flags": flags,
+    }
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+    print(json.dumps({key: db[key]}))
 
 
 def cpu_baseline(wl, seconds: float, gpu_out):
@@ -104,9 +175,12 @@ def cpu_baseline(wl, seconds: float, gpu_out):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -176,6 +250,7 @@ def main():
         kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 else "")
     else:
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
+    # the decode kernel moves almost all bytes; the key lists the step's kernels by traffic
     out_host = out.cpu()
     rec = {
         "metric": METRIC,

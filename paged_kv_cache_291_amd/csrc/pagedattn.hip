@@ -26,8 +26,9 @@
 namespace pa {
 namespace {
 
-// Workgroups of the balanced split per launch (two per CU on 256 CUs).
-constexpr int kSkWorkgroups = 512;
+// Workgroups of the balanced split per launch: one per CU of an MI355X, so
+// all ranges run in one round.
+constexpr int kSkWorkgroups = 256;
 // Largest batch the balanced split handles (its prefix sums live in LDS).
 constexpr int kSkMaxSeqs = 16383;
 

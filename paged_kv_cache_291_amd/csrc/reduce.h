@@ -95,36 +95,65 @@ pa_sk_merge_kernel(void* __restrict__ out, const int* __restrict__ seq_lens, con
   if (w1 == w2) return;                                  // written whole by the decode kernel
   const int kvh = hq / group, hl = hq - kvh * group;
   const int hg = kvh / hpw, wv = kvh - hg * hpw;
-  // One record per workgroup the sequence touched (in range order); workgroups
-  // with an empty range hold none.  The first workgroup's record is its
-  // second slot when its range began in an earlier sequence.
+  // One record per workgroup the sequence touched (in range order); the first
+  // workgroup's record is its second slot when its range began in an earlier
+  // sequence.  Workgroups with an empty range (more workgroups than blocks)
+  // hold none: their weight is zero.
   const int first_begin = sk_range_begin(w1, U, nwg);
   auto rec_of = [&](int w) {
     const int slot = (w == w1 && first_begin < c0) ? 1 : 0;
     return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * group + hl) * REC;
   };
   const int lane = threadIdx.x & 63;
-  float M = -INFINITY;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
   bool nan = false;
-  for (int w = w1; w <= w2; ++w) {
-    if (sk_range_begin(w, U, nwg) == sk_range_begin(w + 1, U, nwg)) continue;
-    const float m = rec_of(w)[0];
-    nan = nan || (m != m);
+  // up to 64 records per pass: lane j reads record w1 + base + j's max and sum
+  float M = -INFINITY;
+  for (int base = w1; base <= w2; base += 64) {
+    const int w = base + lane;
+    const bool live = w <= w2 && sk_range_begin(w, U, nwg) != sk_range_begin(w + 1, U, nwg);
+    const float m = live ? rec_of(w)[0] : -INFINITY;
+    nan = nan || __ballot(m != m);
     M = fmaxf(M, m);
   }
-  float wsum = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) res[e] = 0.f;
-  for (int w = w1; w <= w2; ++w) {
-    if (sk_range_begin(w, U, nwg) == sk_range_begin(w + 1, U, nwg)) continue;
-    const float* r = rec_of(w);
-    const float wp = r[1] * __builtin_amdgcn_exp2f(r[0] - M);
-    wsum += wp;
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  for (int base = w1; base <= w2; base += 64) {
+    const int w = base + lane;
+    const bool live = w <= w2 && sk_range_begin(w, U, nwg) != sk_range_begin(w + 1, U, nwg);
+    const float* r = rec_of(live ? w : w1);
+    const float wl = live ? r[1] * __builtin_amdgcn_exp2f(r[0] - M) : 0.f;   // weight of record `w`
+    wsum += wl;
+    const int n = min(64, w2 - base + 1);
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {                        // four records' loads in flight
+      float o[4][PER], wj[4];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] = fmaf(wp, r[kRecHead + lane * PER + e], res[e]);
+      for (int k = 0; k < 4; ++k) {
+        wj[k] = __shfl(wl, j + k);
+        const float* rk = rec_of(base + j + k);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[k][e] = wj[k] != 0.f ? rk[kRecHead + lane * PER + e] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj[k], o[k][e], acc[e]);
+    }
+    for (; j < n; ++j) {
+      const float wj = __shfl(wl, j);
+      const float* rk = rec_of(base + j);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, wj != 0.f ? rk[kRecHead + lane * PER + e] : 0.f, acc[e]);
+    }
   }
 #pragma unroll
-  for (int e = 0; e < PER; ++e) res[e] = nan ? qnan() : res[e] / wsum;
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) res[e] = nan ? qnan() : acc[e] / wsum;
   write_row<E, D>(out, sh, res);
 }
 
