@@ -69,7 +69,11 @@ __device__ __forceinline__ void mfma_begin(MfmaState<D>& st, const void* query, 
 // Blocks [b_begin, b_end) of one sequence for kv head `kvh`; tokens at or past
 // t_end are masked.  Returns true if a block id of the range is out of the
 // pool (the segment's result is then undefined and must be reported as NaN).
-template <class E, int D, bool NT>
+// LOCK: every wave of the workgroup runs the same segment for its own kv head
+// and the waves meet at a barrier before each block's loads, so the slices of
+// one block's token rows are requested together (DRAM rows stay open for the
+// whole block instead of being reopened by waves that have drifted apart).
+template <class E, int D, bool NT, bool LOCK>
 __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __restrict__ k_cache,
                                              const char* __restrict__ v_cache, const int* __restrict__ bt_row,
                                              int b_begin, int b_end, int t_end, int num_blocks,
@@ -161,16 +165,20 @@ __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __res
     if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) return true;
     const bool last_batch = cb + 64 >= b_end;
     Blk A, B;
+    if constexpr (LOCK) __builtin_amdgcn_s_barrier();
     load_block(__builtin_amdgcn_readlane(id, 0), A);
     int j = 0;
     for (; j + 2 < n; j += 2) {
+      if constexpr (LOCK) __builtin_amdgcn_s_barrier();
       load_block(__builtin_amdgcn_readlane(id, j + 1), B);
       consume(A, BS, false);
+      if constexpr (LOCK) __builtin_amdgcn_s_barrier();
       load_block(__builtin_amdgcn_readlane(id, j + 2), A);
       consume(B, BS, false);
     }
     const int vj = (last_batch && j == n - 1) ? last_valid : BS;
     if (j + 1 < n) {
+      if constexpr (LOCK) __builtin_amdgcn_s_barrier();
       load_block(__builtin_amdgcn_readlane(id, j + 1), B);
       consume(A, BS, false);
       const int vj1 = last_batch ? last_valid : BS;
@@ -251,7 +259,7 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int t_end = bad_len ? 0 : min(L, t_begin + part_tokens);
   bool bad = bad_len;
   if (!bad_len && t_end > t_begin)
-    bad = mfma_segment<E, D, NT>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+    bad = mfma_segment<E, D, NT, false>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
                                  t_begin / BS, ceil_div(t_end, BS), t_end, num_blocks, num_kv_heads, kvh,
                                  qk_scale, lane);
   mfma_finish<E, D, G>(st, bad, out, row0, final_write ? nullptr : ws + (row0 * num_parts + part) * REC,
@@ -351,7 +359,7 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     const int64_t row0 = (int64_t)s * num_heads + kvh * G;
     MfmaState<D> st;
     mfma_begin<D, G>(st, query, row0, lane >> 4, lane & 15);
-    const bool bad = mfma_segment<E, D, NT>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, b0, b1,
+    const bool bad = mfma_segment<E, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, b0, b1,
                                             min(L, b1 * BS), num_blocks, num_kv_heads, kvh, qk_scale, lane);
     const bool whole = b0 == 0 && b1 == c1 - c0;
     float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * G * REC);
