@@ -67,9 +67,10 @@ const char* pa_status_string(int status);
  *    num_seqs * num_heads * ceil(max_seq_len / partition_size) * (head_size + 4) * 4
  *    (one fp32 partial record per partition: max, sum, 2 unused, output)
  *  partition_size == 0 (balanced split, bf16/fp16 KV):
- *    round_up((num_seqs + 1) * 4, 256) + 256 * num_heads * 2 * (head_size + 4) * 4
- *    (prefix sums of blocks per sequence, then two partial records per
- *    workgroup and query head; fp32 KV needs none).
+ *    round_up(num_seqs * 16, 256) + 256 * num_heads * 2 * (head_size + 4) * 4
+ *    (one 16-byte entry per sequence saying where its partial results are,
+ *    then two partial records per range (the work is cut into 256 ranges)
+ *    and query head; fp32 KV needs none).
  * Returns 0 for invalid sizes.  max_seq_len must be the value later passed to
  * paged_attention_decode, or max_blocks_per_seq * block_size if 0 is passed.
  */

@@ -314,9 +314,13 @@ __device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int n
 }
 
 // Grid: head_groups * nwg workgroups of hpw waves (kv heads hg*hpw + wave).
-// Dynamic LDS: (num_seqs + 1) ints.  ws_cum: num_seqs + 1 ints (written by
-// workgroup 0 for the merge kernel); ws_rec: partial records, 2 slots per
-// workgroup (first and last segment of its range) * hpw * G heads.
+// Dynamic LDS: (num_seqs + 1) ints.  ws_seq[s] (written by head group 0):
+// {w1, first block, end block, total blocks} where w1 is the range holding
+// the sequence's first block if the sequence runs past that range's end, -1
+// otherwise (written whole here, or no blocks).  ws_rec: partial records, 2
+// slots per workgroup (first and last segment of its range) * hpw * G heads.
+// Workgroup `rank` also writes the rows of the sequences s = rank (mod nwg)
+// that have no blocks: zeros for length 0, NaN for an out-of-contract length.
 // A workgroup is up to 8 waves; 12 wave slots per CU would still hold only
 // one, so the register budget is that of 2 waves per SIMD.
 template <class E, int D, int G, bool NT>
@@ -325,7 +329,7 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
                     const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                     const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                     int num_seqs, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-                    float qk_scale, int hpw, int nwg, int* __restrict__ ws_cum, float* __restrict__ ws_rec) {
+                    float qk_scale, int hpw, int nwg, int4* __restrict__ ws_seq, float* __restrict__ ws_rec) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
   extern __shared__ int s_cum[];
@@ -337,10 +341,25 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
 
   blocks_prefix_sum(seq_lens, num_seqs, max_blocks, s_cum, s_wsum);
   const int U = s_cum[num_seqs];
-  if (blockIdx.x == 0)
-    for (int i = tid; i <= num_seqs; i += blockDim.x) ws_cum[i] = s_cum[i];
-  if (U == 0) return;
   const int u0 = sk_range_begin(rank, U, nwg), u1 = sk_range_begin(rank + 1, U, nwg);
+  if (hg == 0 && u0 < u1) {
+    int lo = -1, hi = num_seqs;                // first sequence with s_cum[s] >= u0: hi
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cum[mid] >= u0) hi = mid; else lo = mid;
+    }
+    for (int s = hi + tid; s < num_seqs && s_cum[s] < u1; s += blockDim.x) {
+      const int c0 = s_cum[s], c1 = s_cum[s + 1];
+      if (c1 > c0) ws_seq[s] = int4{c1 > u1 ? rank : -1, c0, c1, U};
+    }
+  }
+  for (int s = rank; s < num_seqs; s += nwg) {
+    if (s_cum[s + 1] != s_cum[s]) continue;
+    if (hg == 0 && tid == 0) ws_seq[s] = int4{-1, 0, 0, U};
+    const float v = seq_lens[s] == 0 ? 0.f : qnan();
+    const int64_t e0 = ((int64_t)s * num_heads + kvh * G) * D;
+    for (int i = lane; i < G * D; i += 64) store_elem<E>(out, e0 + i, v);
+  }
   if (u0 >= u1) return;
 
   // first sequence: the last s with s_cum[s] <= u0 (then s_cum[s + 1] > u0)

@@ -61,11 +61,11 @@ size_t split_workspace_bytes(int num_seqs, int num_heads, int head_size, int num
   return (size_t)num_seqs * num_heads * num_parts * (head_size + kRecHead) * sizeof(float);
 }
 
-// Balanced split: prefix sums of blocks per sequence, then two partial
-// records per workgroup per query head it covers.
+// Balanced split: one 16-byte entry per sequence (where its records are),
+// then two partial records per workgroup per query head.
+size_t balanced_seq_bytes(int num_seqs) { return align256((size_t)num_seqs * 16); }
 size_t balanced_workspace_bytes(int num_seqs, int num_heads, int head_size) {
-  return align256((size_t)(num_seqs + 1) * sizeof(int)) +
-         (size_t)kSkWorkgroups * num_heads * 2 * (head_size + kRecHead) * sizeof(float);
+  return balanced_seq_bytes(num_seqs) + (size_t)kSkWorkgroups * num_heads * 2 * (head_size + kRecHead) * sizeof(float);
 }
 
 // Largest divisor of num_kv_heads that is at most 8: kv heads per workgroup.
@@ -102,15 +102,15 @@ int launch_mfma(const Args& a, hipStream_t st) {
   const int hpw = heads_per_workgroup(a.num_kv_heads);
   const int groups = a.num_kv_heads / hpw;
   const int nwg = kSkWorkgroups / groups > 0 ? kSkWorkgroups / groups : 1;
-  int* ws_cum = static_cast<int*>(a.ws);
-  float* ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.ws) + align256((size_t)(a.num_seqs + 1) * sizeof(int)));
+  int4* ws_seq = static_cast<int4*>(a.ws);
+  float* ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.ws) + balanced_seq_bytes(a.num_seqs));
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
   hipLaunchKernelGGL((pa_decode_sk_kernel<E, D, G, NT>), dim3((unsigned)(groups * nwg)), dim3(64 * hpw), lds, st,
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks,
-                     a.num_blocks, a.qk_scale, hpw, nwg, ws_cum, ws_rec);
+                     a.num_blocks, a.qk_scale, hpw, nwg, ws_seq, ws_rec);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  hipLaunchKernelGGL((pa_sk_merge_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
-                     a.out, a.sl, ws_cum, ws_rec, a.num_seqs, a.num_heads, G, hpw, nwg, a.max_blocks);
+  hipLaunchKernelGGL((pa_sk_merge_kernel<E, D, G>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
+                     a.out, ws_seq, ws_rec, a.num_heads, hpw, nwg);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -63,97 +63,109 @@ pa_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws, const int
   write_row<E, D>(out, sh, res);
 }
 
-// Balanced split: one wave per (sequence, query head).  Writes the rows the
-// decode kernel could not: sequences that crossed a range boundary (merged
-// from the records of every workgroup they touched), empty sequences (zero)
-// and out-of-contract lengths (NaN).
-template <class E, int D>
+// Balanced split: one wave per (sequence, query head) of the sequences that
+// ran past the range holding their first block (ws_seq[s] = {w1, first block,
+// end block, total blocks}; w1 = -1: the decode kernel wrote the rows).  Each
+// range the sequence touched left one record per head: the first range's is
+// its second slot when that range began in an earlier sequence; ranges left
+// empty (more workgroups than blocks) hold none.
+template <class E, int D, int G>
 __global__ void __launch_bounds__(64)
-pa_sk_merge_kernel(void* __restrict__ out, const int* __restrict__ seq_lens, const int* __restrict__ ws_cum,
-                   const float* __restrict__ ws_rec, int num_seqs, int num_heads, int group, int hpw, int nwg,
-                   int max_blocks) {
+pa_sk_merge_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, const float* __restrict__ ws_rec,
+                   int num_heads, int hpw, int nwg) {
   constexpr int REC = rec_floats<D>();
   constexpr int PER = D / 64;
-  const int sh = blockIdx.x;
-  const int s = sh / num_heads, hq = sh - s * num_heads;
-  const int L = seq_lens[s];
-  float res[PER];
-  if (L < 0 || (int64_t)L > (int64_t)max_blocks * kBlockSize) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] = qnan();
-    write_row<E, D>(out, sh, res);
-    return;
-  }
-  const int c0 = ws_cum[s], c1 = ws_cum[s + 1], U = ws_cum[num_seqs];
-  if (c0 == c1) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] = 0.f;
-    write_row<E, D>(out, sh, res);
-    return;
-  }
-  const int w1 = sk_owner(c0, U, nwg), w2 = sk_owner(c1 - 1, U, nwg);
-  if (w1 == w2) return;                                  // written whole by the decode kernel
-  const int kvh = hq / group, hl = hq - kvh * group;
+  constexpr int NB = 16;                               // records whose outputs are loaded together
+  const int64_t sh = blockIdx.x;
+  const int s = (int)(sh / num_heads), hq = (int)(sh - (int64_t)s * num_heads);
+  const int4 e = ws_seq[s];
+  if (e.x < 0) return;
+  const int w1 = e.x, c0 = e.y, c1 = e.z, U = e.w;
+  const int n = sk_owner(c1 - 1, U, nwg) - w1 + 1;
+  const int kvh = hq / G, hl = hq - kvh * G;
   const int hg = kvh / hpw, wv = kvh - hg * hpw;
-  // One record per workgroup the sequence touched (in range order); the first
-  // workgroup's record is its second slot when its range began in an earlier
-  // sequence.  Workgroups with an empty range (more workgroups than blocks)
-  // hold none: their weight is zero.
-  const int first_begin = sk_range_begin(w1, U, nwg);
-  auto rec_of = [&](int w) {
-    const int slot = (w == w1 && first_begin < c0) ? 1 : 0;
-    return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * group + hl) * REC;
-  };
   const int lane = threadIdx.x & 63;
-  float acc[PER];
+  const int first_slot = sk_range_begin(w1, U, nwg) < c0 ? 1 : 0;
+  auto rec_of = [&](int j) {                           // record of the sequence's j-th range
+    const int w = w1 + j, slot = j == 0 ? first_slot : 0;
+    return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * G + hl) * REC;
+  };
+  // lane j: is the sequence's record base + j there (its range non-empty)?
+  auto live_lane = [&](int base) {
+    const int j = base + lane;
+    return j < n && sk_range_begin(w1 + j, U, nwg) != sk_range_begin(w1 + j + 1, U, nwg);
+  };
+  auto load_o = [&](uint64_t mask, int base, int k, float* o) {
+    if ((mask >> k) & 1) {
+      const float* r = rec_of(base + k) + kRecHead + lane * PER;
+      if constexpr (PER == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(r);
+        o[0] = v.x; o[1] = v.y;
+      } else {
+        o[0] = r[0];
+      }
+    } else {
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
-  bool nan = false;
-  // up to 64 records per pass: lane j reads record w1 + base + j's max and sum
-  float M = -INFINITY;
-  for (int base = w1; base <= w2; base += 64) {
-    const int w = base + lane;
-    const bool live = w <= w2 && sk_range_begin(w, U, nwg) != sk_range_begin(w + 1, U, nwg);
-    const float m = live ? rec_of(w)[0] : -INFINITY;
-    nan = nan || __ballot(m != m);
+      for (int x = 0; x < PER; ++x) o[x] = 0.f;
+    }
+  };
+
+  // pass 1: maxima (64 records per step; the first step also loads the
+  // outputs of the first NB records)
+  const bool lv0 = live_lane(0);
+  const uint64_t mask0 = __ballot(lv0);
+  float o[NB][PER];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) load_o(mask0, 0, k, o[k]);
+  const float* r0 = rec_of(lv0 ? lane : 0);
+  const float m0 = lv0 ? r0[0] : -INFINITY, l0 = lv0 ? r0[1] : 0.f;
+  bool nan = __ballot(m0 != m0 || l0 != l0) != 0;
+  float M = m0;
+  for (int base = 64; base < n; base += 64) {
+    const bool lv = live_lane(base);
+    const float* r = rec_of(lv ? base + lane : 0);
+    const float m = lv ? r[0] : -INFINITY, l = lv ? r[1] : 0.f;
+    nan = nan || __ballot(m != m || l != l);
     M = fmaxf(M, m);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  for (int base = w1; base <= w2; base += 64) {
-    const int w = base + lane;
-    const bool live = w <= w2 && sk_range_begin(w, U, nwg) != sk_range_begin(w + 1, U, nwg);
-    const float* r = rec_of(live ? w : w1);
-    const float wl = live ? r[1] * __builtin_amdgcn_exp2f(r[0] - M) : 0.f;   // weight of record `w`
+  // pass 2: weighted sum
+  float acc[PER], wsum = 0.f;
+#pragma unroll
+  for (int x = 0; x < PER; ++x) acc[x] = 0.f;
+  for (int base = 0; base < n; base += 64) {
+    bool lv = lv0;
+    uint64_t mask = mask0;
+    float m = m0, l = l0;
+    if (base > 0) {
+      lv = live_lane(base);
+      mask = __ballot(lv);
+      const float* r = rec_of(lv ? base + lane : 0);
+      m = lv ? r[0] : -INFINITY;
+      l = lv ? r[1] : 0.f;
+    }
+    const float wl = lv ? l * __builtin_amdgcn_exp2f(m - M) : 0.f;   // weight of record base + lane
     wsum += wl;
-    const int n = min(64, w2 - base + 1);
-    int j = 0;
-    for (; j + 4 <= n; j += 4) {                        // four records' loads in flight
-      float o[4][PER], wj[4];
+    const int cnt = min(64, n - base);
+    for (int j = 0; j < cnt; j += NB) {
+      if (base > 0 || j > 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        wj[k] = __shfl(wl, j + k);
-        const float* rk = rec_of(base + j + k);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[k][e] = wj[k] != 0.f ? rk[kRecHead + lane * PER + e] : 0.f;
+        for (int k = 0; k < NB; ++k) load_o(mask >> j, base + j, k, o[k]);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < NB; ++k) {
+        const float wk = __shfl(wl, (j + k) & 63);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj[k], o[k][e], acc[e]);
-    }
-    for (; j < n; ++j) {
-      const float wj = __shfl(wl, j);
-      const float* rk = rec_of(base + j);
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, wj != 0.f ? rk[kRecHead + lane * PER + e] : 0.f, acc[e]);
+        for (int x = 0; x < PER; ++x) acc[x] = fmaf(j + k < cnt ? wk : 0.f, o[k][x], acc[x]);
+      }
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+  float res[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) res[e] = nan ? qnan() : acc[e] / wsum;
+  for (int x = 0; x < PER; ++x) res[x] = nan ? qnan() : acc[x] / wsum;
   write_row<E, D>(out, sh, res);
 }
 

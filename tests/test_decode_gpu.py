@@ -160,3 +160,37 @@ def test_contract_violations_give_nan_rows(dtype, ps):
         assert np.isnan(g[s]).all(), s
     ref = oracle_decode(wl, seqs=good)
     assert np.max(np.abs(g[good] - ref)) <= TOL[dtype] + HALF_ULP[dtype] * np.max(np.abs(ref))
+
+
+def _decode_with(wl, ws, ps=0):
+    d = to_device(wl)
+    out = torch.full_like(d["q"], 7.0)                     # every row must be overwritten
+    P.paged_attention_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                             partition_size=ps, max_seq_len=wl.max_seq_len, workspace=ws)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+def test_workspace_reuse_and_empty_batches():
+    """One workspace serves a sequence of different batches: nothing a call
+    leaves in it is read by the next (straddle entries, partial records), and
+    batches with no blocks at all still write every row."""
+    dev = torch.device("cuda")
+    ws = torch.empty(P.pa_decode_workspace_size(1, 32, 128, 0, 0), dtype=torch.uint8, device=dev)
+    lens_a = [3000, 17, 900, 2500, 1, 4100, 640]
+    wa = W.make_random(501, len(lens_a), 32, 8, 128, "bf16", lens_a)
+    lens_b = [40, 1200, 0, 77]
+    wb = W.make_random(502, len(lens_b), 32, 8, 128, "bf16", lens_b)
+    for wl in (wa, wb, wa):
+        g = _decode_with(wl, ws)
+        ref = oracle_decode(wl)
+        assert np.isfinite(g).all()
+        assert float(np.max(np.abs(g - ref) - (TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref)))) <= 0.0
+    empty = W.make_random(503, 5, 32, 8, 128, "bf16", [0, 0, 0, 0, 0])
+    assert (_decode_with(empty, ws) == 0).all()
+    sl = empty.seq_lens.copy()
+    sl[2] = -1                                             # no blocks anywhere, one bad length
+    wbad = W.Workload(**{**empty.__dict__, "seq_lens": sl})
+    g = _decode_with(wbad, ws)
+    assert np.isnan(g[2]).all()
+    assert (np.delete(g, 2, axis=0) == 0).all()
