@@ -225,22 +225,25 @@ __device__ __forceinline__ void mfma_finish(const MfmaState<D>& st, bool bad, vo
   }
 }
 
-// ---- split-context path: one wave per (sequence, kv head, partition)
+// ---- split-context path: one workgroup per (sequence, partition, head
+// group), one wave per kv head of the group (hpw kv heads, as in the balanced
+// split, so a block's heads are read together and the waves run in step).
 // ws: partial records [num_seqs * num_heads * num_parts].
 template <class E, int D, int G, bool NT>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
                       const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                       const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                       int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-                      float qk_scale, int part_tokens, int num_parts, float* __restrict__ ws) {
+                      float qk_scale, int part_tokens, int num_parts, int hpw, float* __restrict__ ws) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
 
   int w = blockIdx.x;
-  const int kvh = w % num_kv_heads;
-  w /= num_kv_heads;
+  const int groups = num_kv_heads / hpw;
+  const int kvh = (w % groups) * hpw + (int)(threadIdx.x >> 6);
+  w /= groups;
   const int part = w % num_parts;
   const int s = w / num_parts;
   const int64_t row0 = (int64_t)s * num_heads + kvh * G;
@@ -259,9 +262,9 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int t_end = bad_len ? 0 : min(L, t_begin + part_tokens);
   bool bad = bad_len;
   if (!bad_len && t_end > t_begin)
-    bad = mfma_segment<E, D, NT, false>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
-                                 t_begin / BS, ceil_div(t_end, BS), t_end, num_blocks, num_kv_heads, kvh,
-                                 qk_scale, lane);
+    bad = mfma_segment<E, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+                                       t_begin / BS, ceil_div(t_end, BS), t_end, num_blocks, num_kv_heads, kvh,
+                                       qk_scale, lane);
   mfma_finish<E, D, G>(st, bad, out, row0, final_write ? nullptr : ws + (row0 * num_parts + part) * REC,
                        (int64_t)num_parts * REC, lane);
 }

@@ -88,12 +88,13 @@ struct Args {
 template <class E, int D, int G, bool NT>
 int launch_mfma(const Args& a, hipStream_t st) {
   if (a.part_tokens > 0) {
-    const long long grid = (long long)a.num_seqs * a.num_parts * a.num_kv_heads;
+    const int hpw = heads_per_workgroup(a.num_kv_heads);
+    const long long grid = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
     if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     float* ws = static_cast<float*>(a.ws);
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<E, D, G, NT>), dim3((unsigned)grid), dim3(64), 0, st,
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<E, D, G, NT>), dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                        a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                       a.num_blocks, a.qk_scale, a.part_tokens, a.num_parts, ws);
+                       a.num_blocks, a.qk_scale, a.part_tokens, a.num_parts, hpw, ws);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
                        a.out, ws, a.sl, a.num_heads, a.max_blocks, a.part_tokens, a.num_parts);

@@ -6,32 +6,86 @@
 
 namespace pa {
 
-// Merge n records (stride in floats) of one (sequence, head) into one output
-// row: M = max_p m_p, w_p = l_p * 2^(m_p - M), out = sum w_p o_p / sum w_p.
-// A NaN record makes the row NaN.  One wave; lane l owns elements PER*l ..
-template <int D, class RecAt>
-__device__ inline void lse_merge(RecAt rec_at, int n, float* res) {
+// Merge the n records of one (sequence, head) into one output row (one wave;
+// lane l owns elements PER*l ..):
+//   M = max_j m_j,  w_j = l_j * 2^(m_j - M),  out = sum_j w_j o_j / sum_j w_j.
+// rec_of(j) is record j; live(j) says whether record j exists (absent records
+// weigh nothing).  A NaN in a record's max or sum makes the row NaN.  Lane j
+// reads the max and sum of record base + j (64 per step); outputs are read NB
+// records at a time, the first NB together with the maxima.
+template <int D, class RecOf, class Live>
+__device__ inline void lse_merge(RecOf rec_of, Live live, int n, float* res) {
   constexpr int PER = D / 64;
+  constexpr int NB = 16;
   const int lane = threadIdx.x & 63;
-  float M = -INFINITY;
-  bool nan = false;
-  for (int p = 0; p < n; ++p) {
-    const float m = rec_at(p)[0];
-    nan = nan || (m != m);
+  auto load_o = [&](uint64_t mask, int j, int k, float* o) {
+    if ((mask >> k) & 1) {
+      const float* r = rec_of(j + k) + kRecHead + lane * PER;
+      if constexpr (PER == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(r);
+        o[0] = v.x; o[1] = v.y;
+      } else {
+        o[0] = r[0];
+      }
+    } else {
+#pragma unroll
+      for (int x = 0; x < PER; ++x) o[x] = 0.f;
+    }
+  };
+  // pass 1: maxima (the first step also loads the first NB records' outputs)
+  const bool lv0 = lane < n && live(lane);
+  const uint64_t mask0 = __ballot(lv0);
+  float o[NB][PER];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) load_o(mask0, 0, k, o[k]);
+  const float* r0 = rec_of(lv0 ? lane : 0);
+  const float m0 = lv0 ? r0[0] : -INFINITY, l0 = lv0 ? r0[1] : 0.f;
+  bool nan = __ballot(m0 != m0 || l0 != l0) != 0;
+  float M = m0;
+  for (int base = 64; base < n; base += 64) {
+    const bool lv = base + lane < n && live(base + lane);
+    const float* r = rec_of(lv ? base + lane : 0);
+    const float m = lv ? r[0] : -INFINITY, l = lv ? r[1] : 0.f;
+    nan = nan || __ballot(m != m || l != l);
     M = fmaxf(M, m);
   }
-  float wsum = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) res[e] = 0.f;
-  for (int p = 0; p < n; ++p) {
-    const float* r = rec_at(p);
-    const float wp = r[1] * __builtin_amdgcn_exp2f(r[0] - M);
-    wsum += wp;
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  // pass 2: weighted sum
+  float acc[PER], wsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] = fmaf(wp, r[kRecHead + lane * PER + e], res[e]);
+  for (int x = 0; x < PER; ++x) acc[x] = 0.f;
+  for (int base = 0; base < n; base += 64) {
+    bool lv = lv0;
+    uint64_t mask = mask0;
+    float m = m0, l = l0;
+    if (base > 0) {
+      lv = base + lane < n && live(base + lane);
+      mask = __ballot(lv);
+      const float* r = rec_of(lv ? base + lane : 0);
+      m = lv ? r[0] : -INFINITY;
+      l = lv ? r[1] : 0.f;
+    }
+    const float wl = lv ? l * __builtin_amdgcn_exp2f(m - M) : 0.f;   // weight of record base + lane
+    wsum += wl;
+    const int cnt = min(64, n - base);
+    for (int j = 0; j < cnt; j += NB) {
+      if (base > 0 || j > 0) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) load_o(mask >> j, base + j, k, o[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float wk = __shfl(wl, (j + k) & 63);
+#pragma unroll
+        for (int x = 0; x < PER; ++x) acc[x] = fmaf(j + k < cnt ? wk : 0.f, o[k][x], acc[x]);
+      }
+    }
   }
 #pragma unroll
-  for (int e = 0; e < PER; ++e) res[e] = nan ? qnan() : res[e] / wsum;
+  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
+#pragma unroll
+  for (int x = 0; x < PER; ++x) res[x] = nan ? qnan() : acc[x] / wsum;
 }
 
 template <class E, int D>
@@ -59,7 +113,7 @@ pa_reduce_kernel(void* __restrict__ out, const float* __restrict__ ws, const int
   if (np <= 1) return;
   const float* base = ws + (int64_t)sh * num_parts * REC;
   float res[D / 64];
-  lse_merge<D>([&](int p) { return base + (int64_t)p * REC; }, np, res);
+  lse_merge<D>([&](int p) { return base + (int64_t)p * REC; }, [](int) { return true; }, np, res);
   write_row<E, D>(out, sh, res);
 }
 
@@ -75,7 +129,6 @@ pa_sk_merge_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, cons
                    int num_heads, int hpw, int nwg) {
   constexpr int REC = rec_floats<D>();
   constexpr int PER = D / 64;
-  constexpr int NB = 16;                               // records whose outputs are loaded together
   const int64_t sh = blockIdx.x;
   const int s = (int)(sh / num_heads), hq = (int)(sh - (int64_t)s * num_heads);
   const int4 e = ws_seq[s];
@@ -90,82 +143,9 @@ pa_sk_merge_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, cons
     const int w = w1 + j, slot = j == 0 ? first_slot : 0;
     return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * G + hl) * REC;
   };
-  // lane j: is the sequence's record base + j there (its range non-empty)?
-  auto live_lane = [&](int base) {
-    const int j = base + lane;
-    return j < n && sk_range_begin(w1 + j, U, nwg) != sk_range_begin(w1 + j + 1, U, nwg);
-  };
-  auto load_o = [&](uint64_t mask, int base, int k, float* o) {
-    if ((mask >> k) & 1) {
-      const float* r = rec_of(base + k) + kRecHead + lane * PER;
-      if constexpr (PER == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(r);
-        o[0] = v.x; o[1] = v.y;
-      } else {
-        o[0] = r[0];
-      }
-    } else {
-#pragma unroll
-      for (int x = 0; x < PER; ++x) o[x] = 0.f;
-    }
-  };
-
-  // pass 1: maxima (64 records per step; the first step also loads the
-  // outputs of the first NB records)
-  const bool lv0 = live_lane(0);
-  const uint64_t mask0 = __ballot(lv0);
-  float o[NB][PER];
-#pragma unroll
-  for (int k = 0; k < NB; ++k) load_o(mask0, 0, k, o[k]);
-  const float* r0 = rec_of(lv0 ? lane : 0);
-  const float m0 = lv0 ? r0[0] : -INFINITY, l0 = lv0 ? r0[1] : 0.f;
-  bool nan = __ballot(m0 != m0 || l0 != l0) != 0;
-  float M = m0;
-  for (int base = 64; base < n; base += 64) {
-    const bool lv = live_lane(base);
-    const float* r = rec_of(lv ? base + lane : 0);
-    const float m = lv ? r[0] : -INFINITY, l = lv ? r[1] : 0.f;
-    nan = nan || __ballot(m != m || l != l);
-    M = fmaxf(M, m);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  // pass 2: weighted sum
-  float acc[PER], wsum = 0.f;
-#pragma unroll
-  for (int x = 0; x < PER; ++x) acc[x] = 0.f;
-  for (int base = 0; base < n; base += 64) {
-    bool lv = lv0;
-    uint64_t mask = mask0;
-    float m = m0, l = l0;
-    if (base > 0) {
-      lv = live_lane(base);
-      mask = __ballot(lv);
-      const float* r = rec_of(lv ? base + lane : 0);
-      m = lv ? r[0] : -INFINITY;
-      l = lv ? r[1] : 0.f;
-    }
-    const float wl = lv ? l * __builtin_amdgcn_exp2f(m - M) : 0.f;   // weight of record base + lane
-    wsum += wl;
-    const int cnt = min(64, n - base);
-    for (int j = 0; j < cnt; j += NB) {
-      if (base > 0 || j > 0) {
-#pragma unroll
-        for (int k = 0; k < NB; ++k) load_o(mask >> j, base + j, k, o[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const float wk = __shfl(wl, (j + k) & 63);
-#pragma unroll
-        for (int x = 0; x < PER; ++x) acc[x] = fmaf(j + k < cnt ? wk : 0.f, o[k][x], acc[x]);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   float res[PER];
-#pragma unroll
-  for (int x = 0; x < PER; ++x) res[x] = nan ? qnan() : acc[x] / wsum;
+  lse_merge<D>(rec_of, [&](int j) { return sk_range_begin(w1 + j, U, nwg) != sk_range_begin(w1 + j + 1, U, nwg); },
+               n, res);
   write_row<E, D>(out, sh, res);
 }
 
