@@ -24,3 +24,11 @@ from .paged_attention import (  # noqa: F401
     lse_combine_ref,
     reshape_and_cache_ref,
 )
+from .block_manager import (  # noqa: F401
+    BlockManagerRef,
+    BlockManagerError,
+    InvalidArg,
+    NoBlocks,
+    Capacity,
+    blocks_for,
+)
