@@ -44,7 +44,9 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad shape relation, misalignment */
   PA_ERR_UNSUPPORTED = -2,  /* dtype / head_size / block_size / group size not built        */
   PA_ERR_WORKSPACE = -3,    /* split path without a large enough workspace                   */
-  PA_ERR_HIP = -4           /* the HIP runtime reported an error at launch                   */
+  PA_ERR_HIP = -4,          /* the HIP runtime reported an error at launch                   */
+  PA_ERR_NO_BLOCKS = -5,    /* block manager: not enough free blocks in the pool             */
+  PA_ERR_CAPACITY = -6      /* block manager: the sequence's table would exceed its maximum  */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -142,6 +144,108 @@ int paged_attention_decode(void* out, const void* query, const void* k_cache, co
 int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                       const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
                       int head_size, int block_size, int num_blocks, int dtype, void* stream);
+
+/*
+ * Copy whole blocks inside both pools (the copies that copy-on-write queues,
+ * see pa_bm_take_copies):
+ *
+ *   for i < num_pairs with src[i], dst[i] in [0, num_blocks):
+ *     k_cache[dst[i]] = k_cache[src[i]];  v_cache[dst[i]] = v_cache[src[i]]
+ *
+ * (one block = block_size * num_kv_heads * head_size elements, copied
+ * bit-exactly).  Pairs naming a block outside the pool are skipped.  The pairs
+ * run in parallel: destinations must be distinct and no block may be both a
+ * source and a destination in one call (true of the copies one batch of
+ * appends queues when no fork happens in between).
+ *
+ *  k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size] (dtype), device
+ *  src, dst         int32 [num_pairs], device
+ */
+int copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int num_pairs,
+                int num_kv_heads, int head_size, int block_size, int num_blocks, int dtype, void* stream);
+
+/*
+ * ---- Block manager (host memory, host calls; no GPU work) ----
+ *
+ * The paged KV cache's bookkeeping (devpress.csdn.net article on the vLLM
+ * architecture, section 1: the KV-cache manager keeps one global pool of free
+ * fixed-size blocks, answers a sequence's requests for blocks, keeps its
+ * logical -> physical block table, and uses reference counts for
+ * copy-on-write so blocks can be shared, e.g. by beam search; section 2 parts
+ * 2 and 4: blocks are taken when a request is scheduled and again when a new
+ * token needs a new block).  Freed blocks are handed out again first
+ * (yangyitao.com vLLM book preface, "from OS to GPU" block-pool figure): the
+ * pool is a stack; a new pool hands out block 0, then 1, 2, ...; a freed
+ * sequence's blocks are pushed in table order.
+ *
+ * Token t of sequence s lives in slot table[t / block_size] * block_size +
+ * t % block_size: the slot_mapping of reshape_and_cache, and (with the tables
+ * from pa_bm_block_tables) the layout paged_attention_decode reads.
+ *
+ * Sequences are ids in [0, max_seqs).  Every call either succeeds or returns
+ * an error and changes nothing.  A manager is not thread-safe; it owns only
+ * host memory, released by pa_bm_destroy.  Slot arrays are host memory owned
+ * by the caller.
+ *
+ * Copy-on-write: appending to a sequence whose last block is partly filled and
+ * shared (reference count > 1) first gives it a fresh block in its place and
+ * queues the pair (shared, fresh); the caller takes the queue
+ * (pa_bm_take_copies), runs copy_blocks on it, and only then writes the new
+ * tokens (reshape_and_cache).  A full shared block is never written, so
+ * appending past it only takes a new block.  A queued copy whose destination
+ * is freed before it is taken is dropped.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager with num_blocks free blocks; *out receives it (NULL on error).
+ * PA_ERR_UNSUPPORTED if num_blocks * block_size does not fit in int32. */
+int pa_bm_create(int num_blocks, int block_size, int max_seqs, int max_blocks_per_seq,
+                 pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* New sequence `seq` (a free id) holding num_tokens tokens: ceil(num_tokens /
+ * block_size) blocks from the pool.  slots (NULL or num_tokens ints) receives
+ * each token's slot.  PA_ERR_NO_BLOCKS / PA_ERR_CAPACITY when they do not fit. */
+int pa_bm_allocate(pa_block_manager* bm, int seq, int num_tokens, int32_t* slots);
+
+/* num_tokens more tokens at the end of `seq`; slots (NULL or num_tokens ints)
+ * receives their slots.  Takes new blocks as the last one fills, after a
+ * copy-on-write of a shared, partly filled last block (see above). */
+int pa_bm_append_slots(pa_block_manager* bm, int seq, int num_tokens, int32_t* slots);
+
+/* New sequence `child` (a free id) sharing every block of `parent`. */
+int pa_bm_fork(pa_block_manager* bm, int parent, int child);
+
+/* Release `seq`: reference counts drop; blocks that reach 0 return to the pool. */
+int pa_bm_free(pa_block_manager* bm, int seq);
+
+/* Free blocks in the pool (>= 0), or an error. */
+int pa_bm_num_free_blocks(const pa_block_manager* bm);
+
+/* The pool, bottom first (the next block handed out is the last one): returns
+ * the count; PA_ERR_INVALID_ARG if capacity is too small. */
+int pa_bm_free_list(const pa_block_manager* bm, int32_t* blocks, int capacity);
+
+/* Reference count of a block, or PA_ERR_INVALID_ARG for an id outside the pool. */
+int pa_bm_ref_count(const pa_block_manager* bm, int block);
+
+/* Tokens held by `seq`, -1 if the id holds no sequence. */
+int pa_bm_seq_len(const pa_block_manager* bm, int seq);
+
+/* The batch seqs[0 .. num_seqs): row i of block_tables ([num_seqs,
+ * max_blocks_per_seq], host) gets seqs[i]'s table padded with -1, and
+ * seq_lens[i] its length: the block_tables / seq_lens of
+ * paged_attention_decode after a copy to the device. */
+int pa_bm_block_tables(const pa_block_manager* bm, const int32_t* seqs, int num_seqs,
+                       int32_t* block_tables, int32_t* seq_lens);
+
+/* Number of queued copies. */
+int pa_bm_num_copies(const pa_block_manager* bm);
+
+/* Move the queued copies (in the order they were queued) into src/dst (host,
+ * capacity entries each) and clear the queue; returns the count.
+ * PA_ERR_INVALID_ARG (nothing taken) if capacity is too small. */
+int pa_bm_take_copies(pa_block_manager* bm, int32_t* src, int32_t* dst, int capacity);
 
 #ifdef __cplusplus
 }

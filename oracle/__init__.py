@@ -23,6 +23,7 @@ from .paged_attention import (  # noqa: F401
     paged_decode_partials_ref,
     lse_combine_ref,
     reshape_and_cache_ref,
+    copy_blocks_ref,
 )
 from .block_manager import (  # noqa: F401
     BlockManagerRef,

@@ -235,3 +235,21 @@ def reshape_and_cache_ref(key, value, k_cache, v_cache, slot_mapping):
         kc[blk, off] = key[i]
         vc[blk, off] = value[i]
     return kc, vc
+
+
+def copy_blocks_ref(k_cache, v_cache, src, dst):
+    """Copy whole blocks in both pools: block ``dst[i]`` becomes a copy of
+    block ``src[i]`` as it was before the call (returns copies).
+
+    csdn section 1: reference counts give copy-on-write, so a shared block is
+    copied before a sequence writes into it.  Pairs naming a block outside the
+    pool are skipped.  Elements are copied as stored (bit-exact).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    nb = kc.shape[0]
+    for s, d in zip(np.asarray(src).tolist(), np.asarray(dst).tolist()):
+        if 0 <= s < nb and 0 <= d < nb:
+            kc[d] = k_cache[s]
+            vc[d] = v_cache[s]
+    return kc, vc

@@ -1,17 +1,23 @@
 """MI355X-native paged decode attention: hand-written HIP for gfx950 behind a C ABI.
 
 Entry points (same names as the C ABI in ``include/pagedattn.h``):
-``paged_attention_decode``, ``reshape_and_cache``, ``pa_decode_workspace_size``,
-``pa_status_string``.  Inputs are torch tensors on a HIP device; torch provides
-memory and streams only.
+``paged_attention_decode``, ``reshape_and_cache``, ``copy_blocks``,
+``pa_decode_workspace_size``, ``pa_status_string``, and ``BlockManager``
+over the host block manager (``pa_bm_*``).  Inputs of the device calls are
+torch tensors on a HIP device; torch provides memory and streams only.
 """
 
 from ._binding import (  # noqa: F401
     DTYPE_CODES,
     EXPORTED,
     LIB_PATH,
+    PA_ERR_CAPACITY,
+    PA_ERR_INVALID_ARG,
+    PA_ERR_NO_BLOCKS,
     PA_FLAG_SHARED_BLOCKS,
+    BlockManager,
     PagedAttnError,
+    copy_blocks,
     decode_workspace_bytes,
     load_library,
     pa_decode_workspace_size,

@@ -18,11 +18,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
+PA_ERR_NO_BLOCKS, PA_ERR_CAPACITY = -5, -6
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_FLAG_SHARED_BLOCKS = 1
 DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
-EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache")
+EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache",
+            "copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_allocate", "pa_bm_append_slots", "pa_bm_fork",
+            "pa_bm_free", "pa_bm_num_free_blocks", "pa_bm_free_list", "pa_bm_ref_count", "pa_bm_seq_len",
+            "pa_bm_block_tables", "pa_bm_num_copies", "pa_bm_take_copies")
 
 _lib = None
 
@@ -54,6 +58,30 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                            c_size, vp]
     lib.reshape_and_cache.restype = c_int
     lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
+    lib.copy_blocks.restype = c_int
+    lib.copy_blocks.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
+    pbm = ctypes.POINTER(vp)
+    lib.pa_bm_create.restype = c_int
+    lib.pa_bm_create.argtypes = [c_int, c_int, c_int, c_int, pbm]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_destroy.argtypes = [vp]
+    for name in ("pa_bm_allocate", "pa_bm_append_slots"):
+        getattr(lib, name).restype = c_int
+        getattr(lib, name).argtypes = [vp, c_int, c_int, vp]
+    lib.pa_bm_fork.restype = c_int
+    lib.pa_bm_fork.argtypes = [vp, c_int, c_int]
+    for name in ("pa_bm_free", "pa_bm_ref_count", "pa_bm_seq_len"):
+        getattr(lib, name).restype = c_int
+        getattr(lib, name).argtypes = [vp, c_int]
+    for name in ("pa_bm_num_free_blocks", "pa_bm_num_copies"):
+        getattr(lib, name).restype = c_int
+        getattr(lib, name).argtypes = [vp]
+    lib.pa_bm_free_list.restype = c_int
+    lib.pa_bm_free_list.argtypes = [vp, vp, c_int]
+    lib.pa_bm_block_tables.restype = c_int
+    lib.pa_bm_block_tables.argtypes = [vp, vp, c_int, vp, vp]
+    lib.pa_bm_take_copies.restype = c_int
+    lib.pa_bm_take_copies.argtypes = [vp, vp, vp, c_int]
     if path is None:
         _lib = lib
     return lib
@@ -159,3 +187,108 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
         _dev(v_cache, "v_cache", dt), _dev(slot_mapping, "slot_mapping", torch.int32), T, Hkv, D, BS,
         NB, DTYPE_CODES[dt], _stream(stream))
     _check(rc)
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
+                stream=None) -> None:
+    """Enqueue block copies ``cache[dst[i]] = cache[src[i]]`` in both pools
+    (int32 device tensors of equal length; see ``include/pagedattn.h``)."""
+    NB, BS, Hkv, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if k_cache.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {k_cache.dtype}")
+    if src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D of equal length")
+    dt = k_cache.dtype
+    rc = load_library().copy_blocks(
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), _dev(src, "src", torch.int32),
+        _dev(dst, "dst", torch.int32), int(src.numel()), Hkv, D, BS, NB, DTYPE_CODES[dt], _stream(stream))
+    _check(rc)
+
+
+class BlockManager:
+    """Host block manager of the paged KV cache (``pa_bm_*`` of the C ABI).
+
+    Sequences are ids in ``[0, max_seqs)``.  Slots, tables and copy lists come
+    back as int32 NumPy arrays in host memory; move them to the device for
+    ``reshape_and_cache`` / ``paged_attention_decode`` / ``copy_blocks``.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, max_seqs: int, max_blocks_per_seq: int):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_bm_create(num_blocks, block_size, max_seqs, max_blocks_per_seq, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.max_seqs, self.max_blocks_per_seq = max_seqs, max_blocks_per_seq
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _slots(self, fn, seq, n):
+        out = self._np.empty(max(n, 0), dtype=self._np.int32)
+        _check(fn(self._h, int(seq), int(n), out.ctypes.data if n > 0 else None))
+        return out
+
+    def allocate(self, seq: int, num_tokens: int):
+        return self._slots(self._lib.pa_bm_allocate, seq, num_tokens)
+
+    def append_slots(self, seq: int, num_tokens: int = 1):
+        return self._slots(self._lib.pa_bm_append_slots, seq, num_tokens)
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free(self, seq: int) -> None:
+        _check(self._lib.pa_bm_free(self._h, int(seq)))
+
+    def num_free_blocks(self) -> int:
+        return self._lib.pa_bm_num_free_blocks(self._h)
+
+    def free_list(self):
+        out = self._np.empty(self.num_blocks, dtype=self._np.int32)
+        n = self._lib.pa_bm_free_list(self._h, out.ctypes.data if self.num_blocks else None, self.num_blocks)
+        if n < 0:
+            _check(n)
+        return out[:n]
+
+    def ref_count(self, block: int) -> int:
+        r = self._lib.pa_bm_ref_count(self._h, int(block))
+        if r < 0:
+            _check(r)
+        return r
+
+    def seq_len(self, seq: int) -> int:
+        r = self._lib.pa_bm_seq_len(self._h, int(seq))
+        if r < -1:
+            _check(r)
+        return r
+
+    def block_tables(self, seqs):
+        np = self._np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        n = int(seqs.size)
+        bt = np.empty((n, self.max_blocks_per_seq), dtype=np.int32)
+        sl = np.empty(n, dtype=np.int32)
+        if n:
+            _check(self._lib.pa_bm_block_tables(self._h, seqs.ctypes.data, n,
+                                                bt.ctypes.data if bt.size else sl.ctypes.data, sl.ctypes.data))
+        return bt, sl
+
+    def take_copies(self):
+        np = self._np
+        n = self._lib.pa_bm_num_copies(self._h)
+        src = np.empty(max(n, 1), dtype=np.int32)
+        dst = np.empty(max(n, 1), dtype=np.int32)
+        got = self._lib.pa_bm_take_copies(self._h, src.ctypes.data, dst.ctypes.data, n)
+        if got < 0:
+            _check(got)
+        return src[:got], dst[:got]

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = [os.path.join(HERE, "csrc", "pagedattn.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "pagedattn.hip"), os.path.join(HERE, "csrc", "block_manager.cpp")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -49,6 +49,39 @@ pa_cache_scatter_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__
   v_cache[dst] = value[src];
 }
 
+// ------------------------------------------------------------ block copies
+
+// Grid (pairs, chunk groups): each thread moves kCopyPerThread 16-byte chunks
+// of the K block and as many of the V block, all loads before all stores.
+constexpr int kCopyPerThread = 4;
+
+__global__ void __launch_bounds__(256)
+pa_copy_blocks_kernel(u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, const int* __restrict__ src,
+                      const int* __restrict__ dst, int block_chunks, int num_blocks) {
+  const int i = blockIdx.x;
+  const int s = src[i], d = dst[i];
+  if ((unsigned)s >= (unsigned)num_blocks || (unsigned)d >= (unsigned)num_blocks) return;
+  const int c0 = blockIdx.y * blockDim.x * kCopyPerThread + threadIdx.x;
+  const int64_t so = (int64_t)s * block_chunks, dof = (int64_t)d * block_chunks;
+  u32x4 k[kCopyPerThread], v[kCopyPerThread];
+#pragma unroll
+  for (int j = 0; j < kCopyPerThread; ++j) {
+    const int c = c0 + j * blockDim.x;
+    if (c < block_chunks) {
+      k[j] = k_cache[so + c];
+      v[j] = v_cache[so + c];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyPerThread; ++j) {
+    const int c = c0 + j * blockDim.x;
+    if (c < block_chunks) {
+      k_cache[dof + c] = k[j];
+      v_cache[dof + c] = v[j];
+    }
+  }
+}
+
 // ------------------------------------------------------------ host side
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -171,6 +204,8 @@ extern "C" const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP launch error";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PA_ERR_CAPACITY: return "block table full";
     default: return "unknown status";
   }
 }
@@ -262,4 +297,25 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
                      (int)chunks, (int64_t)num_blocks * block_size);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
+}
+
+extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int num_pairs,
+                           int num_kv_heads, int head_size, int block_size, int num_blocks, int dtype,
+                           void* stream) {
+  using namespace pa;
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  const long long block_bytes = (long long)block_size * num_kv_heads * head_size * elem_bytes(dtype);
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (block_bytes / 16 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src || !dst) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return PA_ERR_INVALID_ARG;
+  const int chunks = (int)(block_bytes / 16);
+  const int per_group = 256 * kCopyPerThread;
+  const dim3 grid((unsigned)num_pairs, (unsigned)((chunks + per_group - 1) / per_group));
+  hipLaunchKernelGGL(pa_copy_blocks_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), src, dst, chunks, num_blocks);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }

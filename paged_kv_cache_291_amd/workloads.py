@@ -299,3 +299,8 @@ def unshare_prefix(wl: Workload, prefix_blocks: int) -> Workload:
         tables[s, :prefix_blocks] = nb + (s - 1) * prefix_blocks + np.arange(prefix_blocks)
     assert kc.shape[0] == nb + extra
     return replace(wl, k_cache=kc, v_cache=vc, block_tables=tables, name=wl.name + "_private")
+
+
+def random_rows(seed: int, stream: int, shape, dtype: str) -> torch.Tensor:
+    """N(0, 1) tensor of ``shape`` in ``dtype`` from its own seeded stream."""
+    return _normal(np.random.default_rng(np.random.SeedSequence([291, 200, seed, stream])), shape, dtype)

@@ -99,6 +99,17 @@ def test_scatter_host_errors():
     assert f(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 8, 64, 16, 64, 0, None) == -1
 
 
+def test_copy_blocks_host_errors():
+    lib = P.load_library()
+    c = lambda kc=FAKE, vc=FAKE, src=FAKE, dst=FAKE, n=4, Hkv=8, D=128, BS=16, NB=10, dtype=2: \
+        lib.copy_blocks(kc, vc, src, dst, n, Hkv, D, BS, NB, dtype, None)
+    assert c(n=0) == 0                                            # nothing to copy, nothing launched
+    assert c(src=None) == -1 and c(dst=None) == -1 and c(kc=None) == -1
+    assert c(dtype=7) == -1 and c(n=-1) == -1 and c(NB=-1) == -1 and c(Hkv=0) == -1
+    assert c(kc=FAKE + 8) == -1                                   # misaligned pool
+    assert c(Hkv=1, D=1, BS=1, dtype=1) == -2                     # 2-byte blocks: not 16-byte chunks
+
+
 def test_python_binding_refuses_host_tensors():
     q = torch.zeros(2, 4, 64)
     kc = torch.zeros(3, 16, 4, 64)

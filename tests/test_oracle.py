@@ -421,6 +421,27 @@ def test_scatter_then_gather_round_trip():
             assert (oracle.gather_rows(vc2, bt[s], sl[s], kvh)[-1] == value[s, kvh]).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_copy_blocks_matches_elementwise_loop(dtype):
+    rng = np.random.default_rng(21)
+    NB, BS, H, D = 9, 4, 2, 8
+    tdt = W.TORCH_DTYPES[dtype]
+    mk = lambda *s: W.raw_numpy(torch.from_numpy(rng.standard_normal(s).astype(np.float32)).to(tdt))
+    kc, vc = mk(NB, BS, H, D), mk(NB, BS, H, D)
+    src = np.array([1, 4, 0, 2, -1, 3], np.int32)
+    dst = np.array([5, 6, 7, 8, 2, 99], np.int32)     # the last two name blocks outside the pool
+    gk, gv = oracle.copy_blocks_ref(kc, vc, src, dst)
+    wk, wv = kc.copy(), vc.copy()
+    for s_, d_ in [(1, 5), (4, 6), (0, 7), (2, 8)]:
+        for o in range(BS):
+            for h in range(H):
+                for d in range(D):
+                    wk[d_, o, h, d] = kc[s_, o, h, d]
+                    wv[d_, o, h, d] = vc[s_, o, h, d]
+    assert gk.tobytes() == wk.tobytes() and gv.tobytes() == wv.tobytes()
+    assert gk[:5].tobytes() == kc[:5].tobytes()        # sources and the skipped pair's target untouched
+
+
 # ---------------------------------------------------------------- planted mistakes must fail a pin
 
 def _p1_ok():
