@@ -15,6 +15,10 @@ inputs already resident in HBM.  Prints ONE JSON line:
 Workload (default): 8B-shaped GQA decode batch, 256 sequences, 32 query / 8
 kv heads, head_size 128, bf16, block_size 16, lognormal lengths (median 1024,
 sigma 1, clipped to [16, 4096]), shuffled block pool.  Synthetic N(0, 1) data.
+
+Other lines (``--op``): ``copy_blocks`` times the copy-on-write block copies on
+the same pool layout (HBM roofline); ``block_manager`` times the host block
+manager building one decode step of a 256-sequence batch.
 """
 
 from __future__ import annotations
@@ -40,6 +44,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "block_manager"])
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
@@ -173,6 +178,151 @@ def cpu_baseline(wl, seconds: float, gpu_out):
     }, err
 
 
+COPY_PAIRS, COPY_POOL = 4096, 25000
+
+
+def bench_copy_blocks(args):
+    """copy_blocks on the 8B workload's pool layout: 4096 (shared, fresh)
+    pairs of bf16 blocks (16 tokens x 8 kv heads x 128 = 32 KiB per cache)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_291_amd as P
+
+    NB, BS, Hkv, D = COPY_POOL, 16, 8, 128
+    dev = torch.device("cuda:0")
+    kc = torch.zeros((NB, BS, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    ids = np.random.default_rng(np.random.SeedSequence([291, 300, args.seed])).permutation(NB)
+    src = torch.from_numpy(ids[:COPY_PAIRS].astype(np.int32)).to(dev)
+    dst = torch.from_numpy(ids[COPY_PAIRS:2 * COPY_PAIRS].astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        P.copy_blocks(kc, vc, src, dst, stream=stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K = args.steps
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(K):
+        P.copy_blocks(kc, vc, src, dst, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_s = ev0.elapsed_time(ev1) / K / 1e3
+    block_bytes = BS * Hkv * D * 2
+    moved = COPY_PAIRS * 2 * 2 * block_bytes          # K and V blocks, read and written
+    rec = {
+        "metric": "copy_blocks: GB/s moved (read + write) per call",
+        "value": round(moved / (wall / K) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / K, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"copy-on-write copies: {COPY_PAIRS} block pairs of a {NB}-block pool, "
+                               "16 tokens x 8 kv heads x 128 bf16 per block and cache",
+                   "pairs": COPY_PAIRS, "block_bytes_per_cache": block_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(moved / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(moved / launch_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_copy_blocks_kernel", "bytes_per_launch": moved},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from paged_kv_cache_291_amd import workloads as W
+        nb, pairs = 1200, 512
+        k = W.raw_numpy(torch.zeros((nb, BS, Hkv, D), dtype=torch.bfloat16))
+        v = k.copy()
+        sample_ids = np.random.default_rng(1).permutation(nb)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0) or reps == 0:
+            oracle.copy_blocks_ref(k, v, sample_ids[:pairs], sample_ids[pairs:2 * pairs])
+            reps += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(reps * pairs * 2 * 2 * block_bytes / el / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} calls of {pairs} pairs on a {nb}-block pool of the same block "
+                                         f"shape, NumPy, {el:.2f} s"}
+    return rec
+
+
+def bench_block_manager(args):
+    """Host block manager building decode steps of a 256-sequence batch."""
+    import numpy as np
+
+    import paged_kv_cache_291_amd as P
+
+    S, NB, BS, MB = 256, 40000, 16, 512
+    rng = np.random.default_rng(np.random.SeedSequence([291, 301, args.seed]))
+
+    def prompt_len():
+        return int(np.clip(np.round(1024 * np.exp(rng.standard_normal())), 16, 4096))
+
+    # the same trace for the native manager and the oracle: a list of steps
+    K = args.steps
+    trace = []
+    next_id = S
+    live = list(range(S))
+    init = [(s, prompt_len()) for s in live]
+    for k in range(K):
+        ev = []
+        if k % 16 == 15:                                   # 8 finish, 4 new prompts and 4 beams
+            for _ in range(8):
+                ev.append(("free", live.pop(int(rng.integers(len(live))))))
+            for j in range(8):
+                if j < 4:
+                    ev.append(("allocate", next_id, prompt_len()))
+                else:
+                    ev.append(("fork", live[int(rng.integers(len(live)))], next_id))
+                live.append(next_id)
+                next_id = (next_id + 1) % 2048
+                while next_id in live:
+                    next_id = (next_id + 1) % 2048
+        trace.append((ev, list(live)))
+
+    def run(mgr_new, allocate, append, fork, free, take, tables, steps):
+        m = mgr_new()
+        for s, n in init:
+            allocate(m, s, n)
+        t0 = time.perf_counter()
+        for ev, batch in trace[:steps]:
+            for e in ev:
+                if e[0] == "free":
+                    free(m, e[1])
+                elif e[0] == "allocate":
+                    allocate(m, e[1], e[2])
+                else:
+                    fork(m, e[1], e[2])
+            append(m, batch)
+            take(m)
+            tables(m, batch)
+        return time.perf_counter() - t0
+
+    el = run(lambda: P.BlockManager(NB, BS, 2048, MB), lambda m, s, n: m.allocate(s, n),
+             lambda m, b: m.append_batch(b), lambda m, p, c: m.fork(p, c), lambda m, s: m.free(s),
+             lambda m: m.take_copies(), lambda m, b: m.block_tables(b), K)
+    us = el / K * 1e6
+    rec = {
+        "metric": "block manager: host us to build one decode step (appends, copy queue, tables)",
+        "value": round(us, 2), "unit": "us/step", "n_gpus": 0, "steps": K, "warmup": 0,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "serving trace at the 8B batch's scale: 256 live sequences with lognormal "
+                               "prompts (median 1024), one token appended to each per step, every 16 steps "
+                               "8 finish and 4 new prompts + 4 forks arrive; 40000-block pool"},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(K, 64)
+        el_ref = run(lambda: oracle.BlockManagerRef(NB, BS, 2048, MB), lambda m, s, n_: m.allocate(s, n_),
+                     lambda m, b: m.append_batch(b), lambda m, p, c: m.fork(p, c), lambda m, s: m.free_seq(s),
+                     lambda m: m.take_copies(), lambda m, b: m.block_tables(b), n)
+        rec["cpu_baseline"] = {"value": round(el_ref / n * 1e6, 2), "unit": "us/step", "cores": 1,
+                               "kind": "oracle", "sample": f"first {n} steps of the same trace, pure Python"}
+    return rec
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -190,10 +340,16 @@ def main():
     import paged_kv_cache_291_amd as P
     from paged_kv_cache_291_amd import workloads as W
 
+    if args.op == "block_manager":
+        print(json.dumps(bench_block_manager(args)))
+        return
     if not torch.cuda.is_available():
         print("no HIP device visible", file=sys.stderr)
         sys.exit(1)
     P.load_library()
+    if args.op == "copy_blocks":
+        print(json.dumps(bench_copy_blocks(args)))
+        return
     cfg = args.config
     ps = DEFAULT_PARTITION[cfg] if args.partition < 0 else args.partition
     flags = DEFAULT_FLAGS.get(cfg, 0) if args.flags < 0 else args.flags

@@ -213,6 +213,15 @@ int pa_bm_allocate(pa_block_manager* bm, int seq, int num_tokens, int32_t* slots
  * copy-on-write of a shared, partly filled last block (see above). */
 int pa_bm_append_slots(pa_block_manager* bm, int seq, int num_tokens, int32_t* slots);
 
+/* One decode step of a batch: one more token at the end of each seqs[i]
+ * (distinct ids, in order), exactly as num_seqs calls of pa_bm_append_slots
+ * with one token each; slots (NULL or num_seqs ints) receives the slots.  The
+ * whole batch is checked first, so either every sequence grows or nothing
+ * changes: PA_ERR_INVALID_ARG for an id that holds no sequence or appears
+ * twice, else PA_ERR_CAPACITY if a table would exceed its maximum, else
+ * PA_ERR_NO_BLOCKS if the pool cannot cover the new blocks and copies. */
+int pa_bm_append_batch(pa_block_manager* bm, const int32_t* seqs, int num_seqs, int32_t* slots);
+
 /* New sequence `child` (a free id) sharing every block of `parent`. */
 int pa_bm_fork(pa_block_manager* bm, int parent, int child);
 

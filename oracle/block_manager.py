@@ -137,6 +137,24 @@ class BlockManagerRef:
         self.lens[seq] = L + n
         return [self._slot(seq, t) for t in range(L, L + n)]
 
+    def append_batch(self, seqs) -> list[int]:
+        """One more token for each sequence of the batch, in order; all or
+        nothing (the state is restored if any append fails)."""
+        if len(set(seqs)) != len(seqs):
+            raise InvalidArg("duplicate sequence in the batch")
+        for s in seqs:                                     # errors: ids, then capacity, then blocks
+            self._check_live(s)
+        for s in seqs:
+            if blocks_for(self.lens[s] + 1, self.block_size) > self.max_blocks_per_seq:
+                raise Capacity("table full")
+        saved = ({k: list(v) for k, v in self.tables.items()}, dict(self.lens), list(self.free),
+                 list(self.ref), list(self.copies))
+        try:
+            return [self.append_slots(s, 1)[0] for s in seqs]
+        except BlockManagerError:
+            self.tables, self.lens, self.free, self.ref, self.copies = saved
+            raise
+
     def fork(self, parent: int, child: int):
         """child shares every block of parent."""
         self._check_live(parent)

@@ -25,7 +25,7 @@ DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 
 EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache",
             "copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_allocate", "pa_bm_append_slots", "pa_bm_fork",
-            "pa_bm_free", "pa_bm_num_free_blocks", "pa_bm_free_list", "pa_bm_ref_count", "pa_bm_seq_len",
+            "pa_bm_append_batch", "pa_bm_free", "pa_bm_num_free_blocks", "pa_bm_free_list", "pa_bm_ref_count", "pa_bm_seq_len",
             "pa_bm_block_tables", "pa_bm_num_copies", "pa_bm_take_copies")
 
 _lib = None
@@ -68,6 +68,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("pa_bm_allocate", "pa_bm_append_slots"):
         getattr(lib, name).restype = c_int
         getattr(lib, name).argtypes = [vp, c_int, c_int, vp]
+    lib.pa_bm_append_batch.restype = c_int
+    lib.pa_bm_append_batch.argtypes = [vp, vp, c_int, vp]
     lib.pa_bm_fork.restype = c_int
     lib.pa_bm_fork.argtypes = [vp, c_int, c_int]
     for name in ("pa_bm_free", "pa_bm_ref_count", "pa_bm_seq_len"):
@@ -243,6 +245,15 @@ class BlockManager:
 
     def append_slots(self, seq: int, num_tokens: int = 1):
         return self._slots(self._lib.pa_bm_append_slots, seq, num_tokens)
+
+    def append_batch(self, seqs):
+        """One more token for each of ``seqs`` (all or nothing); their slots."""
+        np = self._np
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        out = np.empty(seqs.size, dtype=np.int32)
+        if seqs.size:
+            _check(self._lib.pa_bm_append_batch(self._h, seqs.ctypes.data, int(seqs.size), out.ctypes.data))
+        return out
 
     def fork(self, parent: int, child: int) -> None:
         _check(self._lib.pa_bm_fork(self._h, int(parent), int(child)))

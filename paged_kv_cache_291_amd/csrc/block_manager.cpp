@@ -33,6 +33,8 @@ struct pa_block_manager {
   std::vector<std::vector<int32_t>> tables;        // per sequence id
   std::vector<int32_t> len;                        // tokens per sequence id, -1: no sequence
   std::vector<std::pair<int32_t, int32_t>> copies;
+  std::vector<int32_t> scratch_block;              // per block: pending reference drops (batch check)
+  std::vector<uint8_t> scratch_seq;                // per sequence: seen in the batch
 
   int blocks_for(int64_t tokens) const { return (int)((tokens + block_size - 1) / block_size); }
   bool live(int seq) const { return seq >= 0 && seq < max_seqs && len[seq] >= 0; }
@@ -71,6 +73,8 @@ extern "C" int pa_bm_create(int num_blocks, int block_size, int max_seqs, int ma
     bm->ref.assign(num_blocks, 0);
     bm->tables.resize(max_seqs);
     bm->len.assign(max_seqs, -1);
+    bm->scratch_block.assign(num_blocks, 0);
+    bm->scratch_seq.assign(max_seqs, 0);
   } catch (...) {
     delete bm;
     return PA_ERR_INVALID_ARG;
@@ -127,6 +131,61 @@ extern "C" int pa_bm_append_slots(pa_block_manager* bm, int seq, int num_tokens,
   for (int i = 0; i < grow; ++i) t.push_back(bm->take());
   bm->len[seq] = (int)new_len;
   bm->write_slots(seq, L, num_tokens, slots);
+  return PA_OK;
+}
+
+extern "C" int pa_bm_append_batch(pa_block_manager* bm, const int32_t* seqs, int num_seqs, int32_t* slots) {
+  if (!bm || num_seqs < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!seqs) return PA_ERR_INVALID_ARG;
+  // check the whole batch first, in this order: ids live and distinct, then
+  // table capacity, then enough free blocks for the new blocks and copies
+  // the appends need in order (a shared block copied for one sequence may be
+  // private by the time a later sequence of the batch writes into it)
+  int status = PA_OK;
+  int marked = 0;
+  for (; marked < num_seqs; ++marked) {
+    const int s = seqs[marked];
+    if (!bm->live(s) || bm->scratch_seq[s]) { status = PA_ERR_INVALID_ARG; break; }
+    bm->scratch_seq[s] = 1;
+  }
+  for (int i = 0; i < marked; ++i) bm->scratch_seq[seqs[i]] = 0;
+  if (status != PA_OK) return status;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int L = bm->len[seqs[i]];
+    if (L == 0x7fffffff || bm->blocks_for((int64_t)L + 1) > bm->max_blocks_per_seq) return PA_ERR_CAPACITY;
+  }
+  int64_t need = 0, copies = 0;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int s = seqs[i];
+    const int L = bm->len[s];
+    if (L % bm->block_size == 0) {
+      ++need;
+    } else {
+      const int32_t b = bm->tables[s].back();
+      if (bm->ref[b] - bm->scratch_block[b] > 1) {
+        ++need;
+        ++copies;
+        bm->scratch_block[b] += 1;
+      }
+    }
+  }
+  for (int i = 0; i < num_seqs; ++i) {             // undo the scratch counts
+    const int s = seqs[i];
+    if (bm->len[s] % bm->block_size != 0) bm->scratch_block[bm->tables[s].back()] = 0;
+  }
+  if (need > (int64_t)bm->free_stack.size()) return PA_ERR_NO_BLOCKS;
+  try {
+    bm->copies.reserve(bm->copies.size() + (size_t)copies);
+    for (int i = 0; i < num_seqs; ++i) bm->tables[seqs[i]].reserve(bm->tables[seqs[i]].size() + 1);
+  } catch (...) {
+    return PA_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < num_seqs; ++i) {             // cannot fail now
+    const int s = seqs[i];
+    const int rc = pa_bm_append_slots(bm, s, 1, slots ? slots + i : nullptr);
+    (void)rc;
+  }
   return PA_OK;
 }
 

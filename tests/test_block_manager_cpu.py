@@ -134,3 +134,39 @@ def test_native_large_pool_serving_trace():
             src, dst = m.take_copies()
             assert list(zip(src.tolist(), dst.tolist())) == ref.take_copies()
     same_state(m, ref)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_native_append_batch_matches_oracle(seed):
+    """Batched appends (one token per sequence, all or nothing) against the
+    oracle, including shared partly filled blocks, duplicates and exhaustion."""
+    rng = np.random.default_rng(seed)
+    bs = [1, 4, 16, 2][seed % 4]
+    nb, ms, mb = 24 + 4 * seed, 16, 12
+    nat, ref = P.BlockManager(nb, bs, ms, mb), BlockManagerRef(nb, bs, ms, mb)
+    for op, args in random_trace(500 + seed, 300, ms, bs, 2 * bs):
+        try:
+            ref_op(ref, op, args)
+            native_op(nat, op, args)
+        except BlockManagerError:
+            with pytest.raises(P.PagedAttnError):
+                native_op(nat, op, args)
+        if rng.random() < 0.3 and ref.tables:
+            live = sorted(ref.tables)
+            batch = [int(x) for x in rng.choice(live, size=int(rng.integers(1, len(live) + 1)), replace=False)]
+            if rng.random() < 0.1:
+                batch.append(batch[0])                     # duplicate: refused
+            if rng.random() < 0.05:
+                batch.append(ms - 1 if (ms - 1) not in ref.tables else 0)
+            try:
+                want, status = ref.append_batch(batch), 0
+            except BlockManagerError as e:
+                want, status = None, e.status
+            try:
+                got, got_status = nat.append_batch(batch).tolist(), 0
+            except P.PagedAttnError as e:
+                got, got_status = None, e.status
+            assert (got_status, got) == (status, want), batch
+        src, dst = nat.take_copies()
+        assert list(zip(src.tolist(), dst.tolist())) == ref.take_copies()
+        same_state(nat, ref)

@@ -89,7 +89,8 @@ def test_serving_steps_through_the_manager(dtype, Hq, Hkv, D):
                 write(next_id, mgr.allocate(next_id, L))
                 live.append(next_id)
                 next_id += 1
-        slots = {s: mgr.append_slots(s, 1) for s in live}     # one decode step: a new token each
+        new = mgr.append_batch(live)                           # one decode step: a new token each
+        slots = {s: new[i:i + 1] for i, s in enumerate(live)}
         copies += apply_copies()                               # copy-on-write before the writes
         for s in live:
             write(s, slots[s])

@@ -229,3 +229,33 @@ def test_planted_pool_order_fails_figure():
         seq = ids.setdefault(name, len(ids))
         run_op(m, op, (seq, *rest))
     assert m.block_table(ids["C"]) != g["tables"]["C"]
+
+
+def test_append_batch_is_sequential_appends_or_nothing():
+    import random
+    for seed in range(20):
+        r = random.Random(seed)
+        m = BlockManagerRef(30, 4, 8, 8)
+        for op, args in random_trace(seed, 60, 8, 4, 12):
+            try:
+                run_op(m, op, args)
+            except BlockManagerError:
+                pass
+        live = sorted(m.tables)
+        if not live:
+            continue
+        batch = r.sample(live, r.randint(1, len(live)))
+        seq = copy.deepcopy(m)
+        try:
+            want = [seq.append_slots(s, 1)[0] for s in batch]
+        except BlockManagerError:
+            want = None
+        snap = copy.deepcopy(m.__dict__)
+        try:
+            got = m.append_batch(batch)
+        except BlockManagerError:
+            got = None
+            assert m.__dict__ == snap                      # nothing changed
+        assert got == want
+        if got is not None:
+            assert m.__dict__ == seq.__dict__
