@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--flags", type=int, default=-1, help="decode flags (1 = shared blocks); -1 = workload default")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="capture the decode step in a HIP graph and time replays")
+    ap.add_argument("--graph-calls", type=int, default=1, metavar="N",
+                    help="with --graph: decode calls per captured graph (e.g. one per model layer); "
+                         "times are per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--traffic-from", default="", metavar="FETCH_DIR,WRITE_DIR",
@@ -380,6 +384,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):                  # launches go to the capturing stream
+            for _ in range(args.graph_calls):
+                P.paged_attention_decode(out, q, kc, vc, bt, sl, wl.scale, partition_size=ps,
+                                         max_seq_len=wl.max_seq_len, workspace=ws, flags=flags)
+        stream = torch.cuda.current_stream()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
     K = args.steps
     # Two HIP events on the launch stream bracket the K calls: an event between
     # calls would put its own marker packet (and a gap) between the kernels.
@@ -394,6 +409,9 @@ def main():
     wall = time.perf_counter() - t_start
     launch_ms = np.array([ev0.elapsed_time(ev1) / K])
 
+    calls = args.graph_calls if args.graph else 1      # decode calls per timed replay
+    wall /= calls
+    launch_ms = launch_ms / calls
     kv = wl.kv_bytes()
     ms_per_step = wall * 1e3 / K
     value = kv / (wall / K) / 1e9
@@ -429,6 +447,7 @@ def main():
             "head_size": wl.head_size, "block_size": wl.block_size, "num_blocks": wl.num_blocks,
             "total_tokens": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len,
             "partition_size": ps, "flags": flags, "seed": args.seed, "parallelism": "none (1 GPU)",
+            "launch": f"HIP graph replay, {args.graph_calls} calls per graph" if args.graph else "eager",
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "kv_bytes_per_step": kv,
