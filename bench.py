@@ -45,6 +45,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "block_manager"])
+    ap.add_argument("--kv", default="native", choices=["native", "fp8"],
+                    help="fp8: the same workload over OCP e4m3 pools (random finite codes, scales 1/128 and 1/96)")
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
@@ -151,8 +153,9 @@ def write_traffic(args):
     print(json.dumps({key: db[key]}))
 
 
-def cpu_baseline(wl, seconds: float, gpu_out):
-    """Time the oracle (single thread) on the first sequences of the workload."""
+def cpu_baseline(wl, seconds: float, gpu_out, fp8_pools=None):
+    """Time the oracle (single thread) on the first sequences of the workload
+    (over the fp8 code pools when given)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -160,18 +163,22 @@ def cpu_baseline(wl, seconds: float, gpu_out):
     from paged_kv_cache_291_amd import workloads as W
 
     q, kc, vc = W.raw_numpy(wl.query), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache)
+    extra = {}
+    if fp8_pools is not None:
+        kc, vc = fp8_pools[0].numpy(), fp8_pools[1].numpy()
+        extra = dict(kv_dtype="e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
     done, tok, elapsed, err = 0, 0, 0.0, 0.0
     with threadpool_limits(1):
         while done < wl.num_seqs and elapsed < seconds:
             t0 = time.perf_counter()
             ref = oracle.paged_decode_ref(q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale, wl.dtype,
-                                          seqs=[done])
+                                          seqs=[done], **extra)
             elapsed += time.perf_counter() - t0
             g = gpu_out[done].double().numpy()
             err = max(err, float(np.max(np.abs(g - ref[0]))))
             tok += int(wl.seq_lens[done])
             done += 1
-    kv = tok * wl.num_kv_heads * wl.head_size * 2 * W.ELEM_BYTES[wl.dtype]
+    kv = tok * wl.num_kv_heads * wl.head_size * 2 * (1 if fp8_pools is not None else W.ELEM_BYTES[wl.dtype])
     return {
         "value": round(kv / elapsed / 1e9, 4),
         "unit": "GB/s",
@@ -183,6 +190,7 @@ def cpu_baseline(wl, seconds: float, gpu_out):
 
 
 COPY_PAIRS, COPY_POOL = 4096, 25000
+FP8_K_SCALE, FP8_V_SCALE = 1.0 / 128, 1.0 / 96
 
 
 def bench_copy_blocks(args):
@@ -364,7 +372,16 @@ def main():
           f"tokens={int(wl.seq_lens.sum())} kv_bytes={wl.kv_bytes()}", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     q = wl.query.to(dev)
-    kc, vc = wl.k_cache.to(dev), wl.v_cache.to(dev)
+    fp8 = args.kv == "fp8"
+    if fp8 and wl.dtype == "f32":
+        print("fp8 pools need a bf16 or fp16 query", file=sys.stderr)
+        sys.exit(2)
+    if fp8:
+        kc_host = W.random_fp8_codes(1000 + args.seed, tuple(wl.k_cache.shape))
+        vc_host = W.random_fp8_codes(1001 + args.seed, tuple(wl.v_cache.shape))
+        kc, vc = kc_host.to(dev), vc_host.to(dev)
+    else:
+        kc, vc = wl.k_cache.to(dev), wl.v_cache.to(dev)
     bt = torch.from_numpy(wl.block_tables).to(dev)
     sl = torch.from_numpy(wl.seq_lens).to(dev)
     out = torch.empty_like(q)
@@ -373,13 +390,21 @@ def main():
     if need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if wl.slot_mapping is not None:
-        P.reshape_and_cache(wl.new_key.to(dev), wl.new_value.to(dev), kc, vc,
-                            torch.from_numpy(wl.slot_mapping).to(dev))
+        scatter = (lambda *a: P.reshape_and_cache_fp8(*a, FP8_K_SCALE, FP8_V_SCALE)) if fp8 else P.reshape_and_cache
+        scatter(wl.new_key.to(dev), wl.new_value.to(dev), kc, vc, torch.from_numpy(wl.slot_mapping).to(dev))
     stream = torch.cuda.current_stream()
 
+    def decode(stream_):
+        if fp8:
+            P.paged_attention_decode_fp8(out, q, kc, vc, bt, sl, wl.scale, FP8_K_SCALE, FP8_V_SCALE,
+                                         partition_size=ps, max_seq_len=wl.max_seq_len, workspace=ws, flags=flags,
+                                         stream=stream_)
+        else:
+            P.paged_attention_decode(out, q, kc, vc, bt, sl, wl.scale, partition_size=ps,
+                                     max_seq_len=wl.max_seq_len, workspace=ws, flags=flags, stream=stream_)
+
     def step():
-        P.paged_attention_decode(out, q, kc, vc, bt, sl, wl.scale, partition_size=ps,
-                                 max_seq_len=wl.max_seq_len, workspace=ws, flags=flags, stream=stream)
+        decode(stream)
 
     for _ in range(args.warmup):
         step()
@@ -388,8 +413,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):                  # launches go to the capturing stream
             for _ in range(args.graph_calls):
-                P.paged_attention_decode(out, q, kc, vc, bt, sl, wl.scale, partition_size=ps,
-                                         max_seq_len=wl.max_seq_len, workspace=ws, flags=flags)
+                decode(None)
         stream = torch.cuda.current_stream()
         step = graph.replay
         for _ in range(args.warmup):
@@ -412,7 +436,7 @@ def main():
     calls = args.graph_calls if args.graph else 1      # decode calls per timed replay
     wall /= calls
     launch_ms = launch_ms / calls
-    kv = wl.kv_bytes()
+    kv = wl.kv_bytes() // W.ELEM_BYTES[wl.dtype] if fp8 else wl.kv_bytes()
     ms_per_step = wall * 1e3 / K
     value = kv / (wall / K) / 1e9
     mean_launch_s = float(launch_ms.mean()) / 1e3
@@ -426,6 +450,8 @@ def main():
         kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 else "")
     else:
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
+        if fp8:
+            kernel += "|fp8"
     # the decode kernel moves almost all bytes; the key lists the step's kernels by traffic
     out_host = out.cpu()
     rec = {
@@ -439,10 +465,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype + ("/e4m3 KV" if fp8 else ""),
         "data": "synthetic",
         "config": {
-            "workload": workload,
+            "workload": workload + (", over e4m3 (fp8) K/V pools" if fp8 else ""),
             "num_seqs": wl.num_seqs, "num_heads": wl.num_heads, "num_kv_heads": wl.num_kv_heads,
             "head_size": wl.head_size, "block_size": wl.block_size, "num_blocks": wl.num_blocks,
             "total_tokens": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len,
@@ -466,7 +492,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        cb, err = cpu_baseline(wl, args.cpu_seconds, out_host)
+        cb, err = cpu_baseline(wl, args.cpu_seconds, out_host, (kc_host, vc_host) if fp8 else None)
         rec["cpu_baseline"] = cb
         rec["max_abs_err_vs_oracle_on_cpu_sample"] = err
     if args.copy_calibration > 0:

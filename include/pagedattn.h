@@ -49,7 +49,11 @@ typedef enum {
   PA_ERR_CAPACITY = -6      /* block manager: the sequence's table would exceed its maximum  */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element types.  PA_FP8_E4M3 (OCP 8-bit float, 1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF = NaN, largest finite
+ * 448) is a pool type only: see paged_attention_decode_fp8,
+ * reshape_and_cache_fp8 and copy_blocks. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Flags of paged_attention_decode. */
 enum {
@@ -146,6 +150,47 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
                       int head_size, int block_size, int num_blocks, int dtype, void* stream);
 
 /*
+ * FP8 KV cache.  The pages name quantisation as the way to fit more in less
+ * memory (aiflowlearn.net vLLM course page, quantisation section: several
+ * formats, none spelled out; yangyitao.com vLLM book preface, contents:
+ * quantisation trades precision for speed).  Here the pools hold OCP fp8
+ * e4m3 codes with one scale per pool: a stored code c means e4m3(c) * k_scale
+ * in the K pool and e4m3(c) * v_scale in the V pool.
+ *
+ * paged_attention_decode_fp8 computes exactly what paged_attention_decode
+ * computes, over those values: query and out are dtype (PA_F16 or PA_BF16;
+ * PA_F32 gives PA_ERR_UNSUPPORTED), the pools are [num_blocks, block_size,
+ * num_kv_heads, head_size] bytes.  Codes are widened exactly to dtype in
+ * registers; k_scale enters the score scale and v_scale the final
+ * normalisation.  k_scale and v_scale must be positive and finite.  Every
+ * other argument, the workspace (same size) and the error behaviour are those
+ * of paged_attention_decode.
+ */
+int paged_attention_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                               int block_size, int max_blocks_per_seq, int num_blocks,
+                               int max_seq_len, float scale, float k_scale, float v_scale, int dtype,
+                               int partition_size, unsigned flags, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Scatter with quantisation into fp8 pools: as reshape_and_cache, but each
+ * element x of key (value) is stored as the e4m3 code
+ *
+ *   RNE_e4m3(saturate(x * inv)),  inv = (float)(1.0 / k_scale)  (1.0 / v_scale)
+ *
+ * where x * inv is an fp32 product, saturate clamps to [-448, 448] and keeps
+ * NaN, and RNE_e4m3 rounds to the nearest e4m3 value, ties to the even code.
+ * key/value are dtype (PA_F32, PA_F16 or PA_BF16); num_kv_heads * head_size
+ * must be a multiple of 16.
+ */
+int reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_size,
+                          int block_size, int num_blocks, int dtype, float k_scale, float v_scale,
+                          void* stream);
+
+/*
  * Copy whole blocks inside both pools (the copies that copy-on-write queues,
  * see pa_bm_take_copies):
  *
@@ -158,7 +203,8 @@ int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v
  * source and a destination in one call (true of the copies one batch of
  * appends queues when no fork happens in between).
  *
- *  k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size] (dtype), device
+ *  k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_size] (dtype, any
+ *                   pa_dtype including PA_FP8_E4M3), device
  *  src, dst         int32 [num_pairs], device
  */
 int copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int num_pairs,

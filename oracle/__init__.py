@@ -24,6 +24,10 @@ from .paged_attention import (  # noqa: F401
     lse_combine_ref,
     reshape_and_cache_ref,
     copy_blocks_ref,
+    e4m3_value,
+    E4M3_VALUES,
+    quantize_e4m3_ref,
+    reshape_and_cache_fp8_ref,
 )
 from .block_manager import (  # noqa: F401
     BlockManagerRef,

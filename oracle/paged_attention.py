@@ -73,7 +73,62 @@ def decode_values(raw, dtype: str) -> np.ndarray:
             raise TypeError(f"bf16 data must be 16-bit patterns, got {a.dtype}")
         word = a.view(np.uint16).astype(np.uint32) << np.uint32(16)
         return word.view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        if a.dtype not in (np.uint8, np.int8):
+            raise TypeError(f"e4m3 data must be 8-bit codes, got {a.dtype}")
+        return E4M3_VALUES[a.view(np.uint8)]
     raise ValueError(f"unknown dtype {dtype!r}; expected one of {DTYPES}")
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP 8-bit float E4M3 code (the OCP 8-bit floating point
+    specification's E4M3 encoding): sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6; there are no
+    infinities, and S.1111.111 is NaN, so the largest finite value is
+    1.75 * 2^8 = 448."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_VALUES = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3_ref(x, scale: float) -> np.ndarray:
+    """Codes of ``x / scale`` in E4M3, the way the fp8 pools store them.
+
+    Reading (the pages name quantisation but no format, see the design
+    notes): the product ``x * inv`` is taken in float32 with
+    ``inv = float32(1 / scale)``; values beyond +-448 saturate to +-448; NaN
+    gives the NaN code; everything else rounds to the nearest E4M3 value,
+    ties to the even code (the one whose lowest bit is 0).  ``x`` holds
+    values exactly representable in float32.
+    """
+    inv = np.float32(1.0 / np.float64(scale))
+    y = (np.asarray(x, dtype=np.float64).astype(np.float32) * inv).astype(np.float64)
+    flat = y.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    codes = np.array([c for c in range(256) if not np.isnan(E4M3_VALUES[c])])
+    values = E4M3_VALUES[codes]
+    for i, v in enumerate(flat.tolist()):
+        if v != v:
+            out[i] = 0x7F
+            continue
+        v = min(max(v, -E4M3_MAX), E4M3_MAX)
+        dist = np.abs(values - v)
+        near = codes[dist == dist.min()].tolist()
+        if len(near) > 1:                         # a tie, or +0 / -0
+            signed = [c for c in near if (c & 0x80) == (0x80 if np.signbit(v) else 0)]
+            near = signed or near
+            even = [c for c in near if c % 2 == 0]
+            near = even or near
+        out[i] = near[0]
+    return out.reshape(y.shape)
 
 
 def kv_head_of(h: int, num_heads: int, num_kv_heads: int) -> int:
@@ -130,24 +185,28 @@ def _check_shapes(query, k_cache, v_cache, block_tables, seq_lens):
 
 
 def paged_decode_ref(query, k_cache, v_cache, block_tables, seq_lens, scale: float,
-                     dtype: str, seqs=None) -> np.ndarray:
+                     dtype: str, seqs=None, kv_dtype: str | None = None, k_scale: float = 1.0,
+                     v_scale: float = 1.0) -> np.ndarray:
     """Paged decode attention, float64: csdn section 3, parts 1-2, steps (1)-(5).
 
     For every sequence s (or only those in ``seqs``) and query head h: gather
     the rows of KV head ``kv_head_of(h)`` through the block table, run
     ``softmax_attention`` with ``query[s, h]``, and store the result.
     Returns float64 ``[len(seqs), num_heads, head_size]`` (all sequences when
-    ``seqs`` is None), in the order of ``seqs``.
+    ``seqs`` is None), in the order of ``seqs``.  With ``kv_dtype`` the pools
+    hold that type (``"e4m3"`` codes) and their values are multiplied by
+    ``k_scale`` / ``v_scale``.
     """
     S, Hq, D, NB, BS, Hkv = _check_shapes(query, k_cache, v_cache, block_tables, seq_lens)
     seqs = range(S) if seqs is None else list(seqs)
+    kvt = kv_dtype or dtype
     out = np.zeros((len(seqs), Hq, D), dtype=np.float64)
     for row, s in enumerate(seqs):
         L = int(seq_lens[s])
         q = decode_values(query[s], dtype)                              # [Hq, D]
         for kvh in range(Hkv):
-            K = decode_values(gather_rows(k_cache, block_tables[s], L, kvh), dtype)
-            V = decode_values(gather_rows(v_cache, block_tables[s], L, kvh), dtype)
+            K = decode_values(gather_rows(k_cache, block_tables[s], L, kvh), kvt) * k_scale
+            V = decode_values(gather_rows(v_cache, block_tables[s], L, kvh), kvt) * v_scale
             for h in range(Hq):
                 if kv_head_of(h, Hq, Hkv) == kvh:
                     out[row, h], _ = softmax_attention(q[h], K, V, scale)
@@ -253,3 +312,14 @@ def copy_blocks_ref(k_cache, v_cache, src, dst):
             kc[d] = k_cache[s]
             vc[d] = v_cache[s]
     return kc, vc
+
+
+def reshape_and_cache_fp8_ref(key, value, k_cache, v_cache, slot_mapping, dtype: str, k_scale: float,
+                              v_scale: float):
+    """Scatter with quantisation: as ``reshape_and_cache_ref``, but the rows
+    of ``key`` / ``value`` (stored as ``dtype``) are written as E4M3 codes of
+    ``x / k_scale`` / ``x / v_scale`` (``quantize_e4m3_ref``).  Returns copies
+    of the code pools."""
+    kq = quantize_e4m3_ref(decode_values(key, dtype), k_scale)
+    vq = quantize_e4m3_ref(decode_values(value, dtype), v_scale)
+    return reshape_and_cache_ref(kq, vq, k_cache, v_cache, slot_mapping)

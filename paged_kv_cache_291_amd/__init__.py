@@ -1,7 +1,8 @@
 """MI355X-native paged decode attention: hand-written HIP for gfx950 behind a C ABI.
 
 Entry points (same names as the C ABI in ``include/pagedattn.h``):
-``paged_attention_decode``, ``reshape_and_cache``, ``copy_blocks``,
+``paged_attention_decode``, ``reshape_and_cache``, ``paged_attention_decode_fp8``,
+``reshape_and_cache_fp8``, ``copy_blocks``,
 ``pa_decode_workspace_size``, ``pa_status_string``, and ``BlockManager``
 over the host block manager (``pa_bm_*``).  Inputs of the device calls are
 torch tensors on a HIP device; torch provides memory and streams only.
@@ -15,6 +16,7 @@ from ._binding import (  # noqa: F401
     PA_ERR_INVALID_ARG,
     PA_ERR_NO_BLOCKS,
     PA_FLAG_SHARED_BLOCKS,
+    PA_FP8_E4M3,
     BlockManager,
     PagedAttnError,
     copy_blocks,
@@ -23,5 +25,7 @@ from ._binding import (  # noqa: F401
     pa_decode_workspace_size,
     pa_status_string,
     paged_attention_decode,
+    paged_attention_decode_fp8,
     reshape_and_cache,
+    reshape_and_cache_fp8,
 )

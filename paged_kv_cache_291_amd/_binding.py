@@ -19,11 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
 PA_ERR_NO_BLOCKS, PA_ERR_CAPACITY = -5, -6
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_FLAG_SHARED_BLOCKS = 1
 DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+# fp8 pools: raw e4m3 codes as uint8, or torch's float8_e4m3fn (the same encoding)
+FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache",
+            "paged_attention_decode_fp8", "reshape_and_cache_fp8",
             "copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_allocate", "pa_bm_append_slots", "pa_bm_fork",
             "pa_bm_append_batch", "pa_bm_free", "pa_bm_num_free_blocks", "pa_bm_free_list", "pa_bm_ref_count", "pa_bm_seq_len",
             "pa_bm_block_tables", "pa_bm_num_copies", "pa_bm_take_copies")
@@ -58,6 +61,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                            c_size, vp]
     lib.reshape_and_cache.restype = c_int
     lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
+    lib.paged_attention_decode_fp8.restype = c_int
+    lib.paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
+                                               c_int, c_int, c_int, c_float, c_float, c_float, c_int, c_int,
+                                               ctypes.c_uint, vp, c_size, vp]
+    lib.reshape_and_cache_fp8.restype = c_int
+    lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                                          c_float, vp]
     lib.copy_blocks.restype = c_int
     lib.copy_blocks.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
     pbm = ctypes.POINTER(vp)
@@ -191,6 +201,63 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     _check(rc)
 
 
+def _fp8_pool(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in FP8_POOL_DTYPES:
+        raise TypeError(f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    return _dev(t, name)
+
+
+def paged_attention_decode_fp8(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                               v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                               scale: float, k_scale: float, v_scale: float, partition_size: int = 0,
+                               max_seq_len: int = 0, workspace: Optional[torch.Tensor] = None, flags: int = 0,
+                               stream=None) -> torch.Tensor:
+    """Decode over fp8 (e4m3) pools: a code c means e4m3(c) * k_scale (K) or
+    * v_scale (V).  query/out are bf16 or fp16; everything else is as in
+    ``paged_attention_decode``."""
+    S, Hq, D = query.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between out/query/k_cache/v_cache")
+    if query.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"query must be fp16 or bf16, got {query.dtype}")
+    dt = query.dtype
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and seq_lens [S]")
+    ws_ptr, ws_bytes = 0, 0
+    need = decode_workspace_bytes(query, block_tables, BS, partition_size, max_seq_len)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    rc = load_library().paged_attention_decode_fp8(
+        _dev(out, "out", dt), _dev(query, "query", dt), _fp8_pool(k_cache, "k_cache"), _fp8_pool(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), _dev(seq_lens, "seq_lens", torch.int32), S, Hq, Hkv, D,
+        BS, block_tables.shape[1], NB, int(max_seq_len), float(scale), float(k_scale), float(v_scale),
+        DTYPE_CODES[dt], int(partition_size), int(flags), ws_ptr, ws_bytes, _stream(stream))
+    _check(rc)
+    return out
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          slot_mapping: torch.Tensor, k_scale: float, v_scale: float, stream=None) -> None:
+    """Enqueue the scatter of ``key``/``value`` ``[T, Hkv, D]`` (fp32/fp16/bf16)
+    into fp8 pools, quantised as in ``include/pagedattn.h``."""
+    T, Hkv, D = key.shape
+    NB, BS, Hkv2, D2 = k_cache.shape
+    if tuple(value.shape) != (T, Hkv, D) or (Hkv2, D2) != (Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between key/value and the caches")
+    if key.dtype not in DTYPE_CODES or value.dtype != key.dtype:
+        raise TypeError(f"unsupported dtype {key.dtype}")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    rc = load_library().reshape_and_cache_fp8(
+        _dev(key, "key", key.dtype), _dev(value, "value", key.dtype), _fp8_pool(k_cache, "k_cache"),
+        _fp8_pool(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32), T, Hkv, D, BS, NB,
+        DTYPE_CODES[key.dtype], float(k_scale), float(v_scale), _stream(stream))
+    _check(rc)
+
+
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
                 stream=None) -> None:
     """Enqueue block copies ``cache[dst[i]] = cache[src[i]]`` in both pools
@@ -198,14 +265,15 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor,
     NB, BS, Hkv, D = k_cache.shape
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache must match")
-    if k_cache.dtype not in DTYPE_CODES:
+    if k_cache.dtype not in DTYPE_CODES and k_cache.dtype not in FP8_POOL_DTYPES:
         raise TypeError(f"unsupported dtype {k_cache.dtype}")
     if src.shape != dst.shape or src.dim() != 1:
         raise ValueError("src and dst must be 1-D of equal length")
     dt = k_cache.dtype
+    code = DTYPE_CODES.get(dt, PA_FP8_E4M3)
     rc = load_library().copy_blocks(
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), _dev(src, "src", torch.int32),
-        _dev(dst, "dst", torch.int32), int(src.numel()), Hkv, D, BS, NB, DTYPE_CODES[dt], _stream(stream))
+        _dev(dst, "dst", torch.int32), int(src.numel()), Hkv, D, BS, NB, code, _stream(stream))
     _check(rc)
 
 

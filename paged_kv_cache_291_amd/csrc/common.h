@@ -1,6 +1,8 @@
 // Device helpers shared by the paged decode kernels (gfx950, 64-lane waves).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -196,6 +198,22 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
 template <bool NT>
 __device__ inline u32x2 load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, NT ? 2 : 0);
+}
+
+template <bool NT>
+__device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, NT ? 2 : 0);
+}
+
+// Two OCP fp8 e4m3 values (bytes 0-1, or 2-3 when `hi`) of a dword as two
+// 16-bit values of type E in one dword.  Every e4m3 value is exact in bf16
+// and fp16, so this conversion is exact.
+template <class E, bool HI>
+__device__ inline uint32_t fp8x2_to(uint32_t w) {
+  if constexpr (E::kBytes == 2 && std::is_same<E, ElemBF16>::value)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
 }
 
 // ------------------------------------------------------------ lane exchange

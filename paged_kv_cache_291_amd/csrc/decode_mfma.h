@@ -53,13 +53,96 @@ struct MfmaState {
   f32x4 acc[MfmaShape<D>::kVe];   // O[h = 4*(l/16) + i][d = VE*(l%16) + T]
 };
 
-template <int D, int G>
+// Formats of the K/V pools.  Kv16: elements of the query type (bf16 or
+// fp16).  KvFp8: OCP fp8 e4m3 codes, dequantised in registers to the query
+// type (exactly: every e4m3 value is a bf16 and an fp16 value); the pools'
+// scales enter the score scale (K) and the final normalisation (V).
+struct Kv16 { static constexpr int kBytes = 2; };
+struct KvFp8 { static constexpr int kBytes = 1; };
+
+// Where each lane's K/V bytes are and how they become MFMA operands.  For a
+// QK step the lane (c = l%16, g = l/16) supplies 8 consecutive elements of K
+// row c; which 8 (the map d(g, step)) only has to agree with the query
+// operand, since QK sums over d.
+template <class KV, class E, int D>
+struct KvIo;
+
+template <class E, int D>
+struct KvIo<Kv16, E, D> {
+  using SH = MfmaShape<D>;
+  static constexpr int kRowBytes = D * 2;
+  struct Blk {
+    u32x4 k[SH::kKs];                 // K row c, d = 32*step + 8*g ..
+    uint32_t v[4][SH::kVw];           // V rows 4*g + j, d = VE*c ..
+  };
+  __device__ static int q_elem(int g, int step) { return 32 * step + 8 * g; }
+  __device__ static int k_off(int c, int g, int hkv, int kvh) { return (c * hkv + kvh) * kRowBytes + 16 * g; }
+  __device__ static int v_off(int c, int g, int hkv, int kvh) { return (4 * g * hkv + kvh) * kRowBytes + SH::kVe * 2 * c; }
+  template <bool NT>
+  __device__ static void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k_off, int v_off,
+                              int row_stride, Blk& b) {
+#pragma unroll
+    for (int k = 0; k < SH::kKs; ++k) b.k[k] = load16<NT>(rk, k_off, 64 * k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (SH::kVw == 4) {
+        const u32x4 t = load16<NT>(rv, v_off, j * row_stride);
+        b.v[j][0] = t[0]; b.v[j][1] = t[1]; b.v[j][2] = t[2]; b.v[j][3] = t[3];
+      } else {
+        const u32x2 t = load8<NT>(rv, v_off, j * row_stride);
+        b.v[j][0] = t[0]; b.v[j][1] = t[1];
+      }
+    }
+  }
+  __device__ static u32x4 k_operand(const Blk& b, int step) { return b.k[step]; }
+  __device__ static uint32_t v_word(const Blk& b, int j, int q) { return b.v[j][q]; }
+};
+
+template <class E, int D>
+struct KvIo<KvFp8, E, D> {
+  using SH = MfmaShape<D>;
+  static constexpr int kRowBytes = D;
+  static constexpr int kKq = D / 64;  // 16-byte K loads per lane (its D/4 contiguous codes)
+  static constexpr int kVq = SH::kVe / 4;   // dwords of V codes per row per lane
+  struct Blk {
+    u32x4 k[kKq];                     // K row c, d = (D/4)*g .. (D/4)*g + D/4 - 1
+    uint32_t v[4][kVq];               // V rows 4*g + j, d = VE*c ..
+  };
+  __device__ static int q_elem(int g, int step) { return (D / 4) * g + 8 * step; }
+  __device__ static int k_off(int c, int g, int hkv, int kvh) { return (c * hkv + kvh) * kRowBytes + (D / 4) * g; }
+  __device__ static int v_off(int c, int g, int hkv, int kvh) { return (4 * g * hkv + kvh) * kRowBytes + SH::kVe * c; }
+  template <bool NT>
+  __device__ static void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int k_off, int v_off,
+                              int row_stride, Blk& b) {
+#pragma unroll
+    for (int k = 0; k < kKq; ++k) b.k[k] = load16<NT>(rk, k_off, 16 * k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kVq == 2) {
+        const u32x2 t = load8<NT>(rv, v_off, j * row_stride);
+        b.v[j][0] = t[0]; b.v[j][1] = t[1];
+      } else {
+        b.v[j][0] = load4<NT>(rv, v_off, j * row_stride);
+      }
+    }
+  }
+  __device__ static u32x4 k_operand(const Blk& b, int step) {
+    const uint32_t w0 = b.k[step >> 1][(2 * step) & 3], w1 = b.k[step >> 1][(2 * step + 1) & 3];
+    return u32x4{fp8x2_to<E, false>(w0), fp8x2_to<E, true>(w0), fp8x2_to<E, false>(w1), fp8x2_to<E, true>(w1)};
+  }
+  __device__ static uint32_t v_word(const Blk& b, int j, int q) {   // q is unrolled: the branch folds
+    return (q & 1) ? fp8x2_to<E, true>(b.v[j][q >> 1]) : fp8x2_to<E, false>(b.v[j][q >> 1]);
+  }
+};
+
+template <class KV, int D, int G>
 __device__ __forceinline__ void mfma_begin(MfmaState<D>& st, const void* query, int64_t q_row0, int g, int c) {
   using SH = MfmaShape<D>;
-  const char* qrow = static_cast<const char*>(query) + (q_row0 + c) * SH::kRow + 16 * g;
+  using IO = KvIo<KV, ElemBF16, D>;              // the query map does not depend on E
+  const char* qrow = static_cast<const char*>(query) + (q_row0 + c) * SH::kRow;
 #pragma unroll
   for (int k = 0; k < SH::kKs; ++k)
-    st.qb[k] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 64 * k) : u32x4{0u, 0u, 0u, 0u};
+    st.qb[k] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 2 * IO::q_elem(g, k)) : u32x4{0u, 0u, 0u, 0u};
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
 #pragma unroll
@@ -73,46 +156,32 @@ __device__ __forceinline__ void mfma_begin(MfmaState<D>& st, const void* query, 
 // and the waves meet at a barrier before each block's loads, so the slices of
 // one block's token rows are requested together (DRAM rows stay open for the
 // whole block instead of being reopened by waves that have drifted apart).
-template <class E, int D, bool NT, bool LOCK>
+template <class E, class KV, int D, bool NT, bool LOCK>
 __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __restrict__ k_cache,
                                              const char* __restrict__ v_cache, const int* __restrict__ bt_row,
                                              int b_begin, int b_end, int t_end, int num_blocks,
                                              int num_kv_heads, int kvh, float qk_scale, int lane) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
+  using IO = KvIo<KV, E, D>;
+  using Blk = typename IO::Blk;
   constexpr int BS = kBlockSize, KS = SH::kKs, VE = SH::kVe, VW = SH::kVw;
   const int g = lane >> 4, c = lane & 15;
-  const int blk_bytes = BS * num_kv_heads * SH::kRow;
-  const int row_stride = num_kv_heads * SH::kRow;
-  const int k_off = (c * num_kv_heads + kvh) * SH::kRow + 16 * g;             // K row t = l%16
-  const int v_off = (4 * g * num_kv_heads + kvh) * SH::kRow + VE * 2 * c;     // V row t = 4*(l/16) + j
-
-  struct Blk {
-    u32x4 k[KS];
-    uint32_t v[4][VW];
-  };
+  const int blk_bytes = BS * num_kv_heads * IO::kRowBytes;
+  const int row_stride = num_kv_heads * IO::kRowBytes;
+  const int k_off = IO::k_off(c, g, num_kv_heads, kvh);     // K row t = l%16
+  const int v_off = IO::v_off(c, g, num_kv_heads, kvh);     // V rows t = 4*(l/16) + j
 
   auto load_block = [&](int phys, Blk& b) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(k_cache + (int64_t)phys * blk_bytes, blk_bytes);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(v_cache + (int64_t)phys * blk_bytes, blk_bytes);
-#pragma unroll
-    for (int k = 0; k < KS; ++k) b.k[k] = load16<NT>(rk, k_off, 64 * k);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (VW == 4) {
-        const u32x4 t = load16<NT>(rv, v_off, j * row_stride);
-        b.v[j][0] = t[0]; b.v[j][1] = t[1]; b.v[j][2] = t[2]; b.v[j][3] = t[3];
-      } else {
-        const u32x2 t = load8<NT>(rv, v_off, j * row_stride);
-        b.v[j][0] = t[0]; b.v[j][1] = t[1];
-      }
-    }
+    IO::template load<NT>(rk, rv, k_off, v_off, row_stride, b);
   };
 
   auto consume = [&](const Blk& b, int valid, bool masked) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < KS; ++k) sc = M::qk(b.k[k], st.qb[k], sc);
+    for (int k = 0; k < KS; ++k) sc = M::qk(IO::k_operand(b, k), st.qb[k], sc);
     float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -143,7 +212,7 @@ __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < VW; ++q) v[j][q] = (masked && 4 * g + j >= valid) ? 0u : b.v[j][q];
+      for (int q = 0; q < VW; ++q) v[j][q] = (masked && 4 * g + j >= valid) ? 0u : IO::v_word(b, j, q);
 #pragma unroll
     for (int T = 0; T < VE; ++T) {
       const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;   // high or low half of each dword
@@ -198,7 +267,7 @@ __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __res
 template <class E, int D, int G>
 __device__ __forceinline__ void mfma_finish(const MfmaState<D>& st, bool bad, void* __restrict__ out,
                                             int64_t out_row0, float* __restrict__ rec, int64_t rec_stride,
-                                            int lane) {
+                                            float out_scale, int lane) {
   constexpr int VE = MfmaShape<D>::kVe;
   const int g = lane >> 4, c = lane & 15;
   const float l_head = rows_sum(st.l_part);                 // softmax sum of head l%16
@@ -208,7 +277,7 @@ __device__ __forceinline__ void mfma_finish(const MfmaState<D>& st, bool bad, vo
     const float lh = __shfl(l_head, h);
     const float mh = __shfl(st.m_ref, h);
     if (h >= G) continue;
-    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const float inv = lh > 0.f ? out_scale / lh : 0.f;
     float o[VE];
 #pragma unroll
     for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
@@ -229,13 +298,14 @@ __device__ __forceinline__ void mfma_finish(const MfmaState<D>& st, bool bad, vo
 // group), one wave per kv head of the group (hpw kv heads, as in the balanced
 // split, so a block's heads are read together and the waves run in step).
 // ws: partial records [num_seqs * num_heads * num_parts].
-template <class E, int D, int G, bool NT>
+template <class E, class KV, int D, int G, bool NT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
                       const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                       const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                       int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-                      float qk_scale, int part_tokens, int num_parts, int hpw, float* __restrict__ ws) {
+                      float qk_scale, float v_scale, int part_tokens, int num_parts, int hpw,
+                      float* __restrict__ ws) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
   const int lane = threadIdx.x & 63;
@@ -249,7 +319,7 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int64_t row0 = (int64_t)s * num_heads + kvh * G;
 
   MfmaState<D> st;
-  mfma_begin<D, G>(st, query, row0, lane >> 4, lane & 15);
+  mfma_begin<KV, D, G>(st, query, row0, lane >> 4, lane & 15);
 
   const int L = seq_lens[s];
   const int64_t cap = min((int64_t)max_blocks * BS, (int64_t)num_parts * part_tokens);
@@ -262,11 +332,11 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int t_end = bad_len ? 0 : min(L, t_begin + part_tokens);
   bool bad = bad_len;
   if (!bad_len && t_end > t_begin)
-    bad = mfma_segment<E, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+    bad = mfma_segment<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
                                        t_begin / BS, ceil_div(t_end, BS), t_end, num_blocks, num_kv_heads, kvh,
                                        qk_scale, lane);
   mfma_finish<E, D, G>(st, bad, out, row0, final_write ? nullptr : ws + (row0 * num_parts + part) * REC,
-                       (int64_t)num_parts * REC, lane);
+                       (int64_t)num_parts * REC, v_scale, lane);
 }
 
 // ---- balanced split (stream-K over the batch's blocks)
@@ -326,13 +396,14 @@ __device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int n
 // that have no blocks: zeros for length 0, NaN for an out-of-contract length.
 // A workgroup is up to 8 waves; 12 wave slots per CU would still hold only
 // one, so the register budget is that of 2 waves per SIMD.
-template <class E, int D, int G, bool NT>
+template <class E, class KV, int D, int G, bool NT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
                     const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                     const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                     int num_seqs, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-                    float qk_scale, int hpw, int nwg, int4* __restrict__ ws_seq, float* __restrict__ ws_rec) {
+                    float qk_scale, float v_scale, int hpw, int nwg, int4* __restrict__ ws_seq,
+                    float* __restrict__ ws_rec) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
   extern __shared__ int s_cum[];
@@ -380,12 +451,12 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     const int L = seq_lens[s];
     const int64_t row0 = (int64_t)s * num_heads + kvh * G;
     MfmaState<D> st;
-    mfma_begin<D, G>(st, query, row0, lane >> 4, lane & 15);
-    const bool bad = mfma_segment<E, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, b0, b1,
+    mfma_begin<KV, D, G>(st, query, row0, lane >> 4, lane & 15);
+    const bool bad = mfma_segment<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, b0, b1,
                                             min(L, b1 * BS), num_blocks, num_kv_heads, kvh, qk_scale, lane);
     const bool whole = b0 == 0 && b1 == c1 - c0;
     float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * G * REC);
-    mfma_finish<E, D, G>(st, bad, out, row0, rec, REC, lane);
+    mfma_finish<E, D, G>(st, bad, out, row0, rec, REC, v_scale, lane);
     u += b1 - b0;
     ++s;
   }

@@ -49,6 +49,45 @@ pa_cache_scatter_kernel(const u32x4* __restrict__ key, const u32x4* __restrict__
   v_cache[dst] = value[src];
 }
 
+// Scatter with quantisation to OCP fp8 e4m3: one thread per 16 elements of a
+// token's row.  code = RNE_e4m3(saturate(x * inv_scale)), where x * inv_scale
+// is an fp32 product, saturate clamps to the format's finite range +-448 and
+// keeps NaN, and the rounding is the hardware's (nearest, ties to even).
+constexpr float kFp8Max = 448.0f;
+
+__device__ inline float fp8_saturate(float y) { return y > kFp8Max ? kFp8Max : (y < -kFp8Max ? -kFp8Max : y); }
+
+template <class E>
+__global__ void __launch_bounds__(256)
+pa_cache_scatter_fp8_kernel(const char* __restrict__ key, const char* __restrict__ value,
+                            u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache,
+                            const int* __restrict__ slot_mapping, int row_chunks, int64_t num_slots,
+                            float inv_k, float inv_v) {
+  const int t = blockIdx.x;
+  const int chunk = blockIdx.y * blockDim.x + threadIdx.x;
+  if (chunk >= row_chunks) return;
+  const int slot = slot_mapping[t];
+  if (slot < 0 || (int64_t)slot >= num_slots) return;
+  const int64_t src = ((int64_t)t * row_chunks + chunk) * 16 * E::kBytes;
+  const int64_t dst = (int64_t)slot * row_chunks + chunk;
+  auto quantise = [&](const char* base, float inv) {
+    float x[16];
+    const u32x4* in = reinterpret_cast<const u32x4*>(base + src);
+#pragma unroll
+    for (int i = 0; i < E::kBytes; ++i) widen16<E>(in[i], x + i * (16 / E::kBytes));
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_saturate(x[4 * w] * inv), fp8_saturate(x[4 * w + 1] * inv), 0, false);
+      out[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_saturate(x[4 * w + 2] * inv),
+                                                         fp8_saturate(x[4 * w + 3] * inv), lo, true);
+    }
+    return out;
+  };
+  k_cache[dst] = quantise(key, inv_k);
+  v_cache[dst] = quantise(value, inv_v);
+}
+
 // ------------------------------------------------------------ block copies
 
 // Grid (pairs, chunk groups): each thread moves kCopyPerThread 16-byte chunks
@@ -89,7 +128,7 @@ pa_copy_blocks_kernel(u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, 
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -115,22 +154,22 @@ struct Args {
   void* out; const void* query; const char* kc; const char* vc;
   const int* bt; const int* sl;
   int num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks;
-  float qk_scale;
+  float qk_scale, v_scale;
   int part_tokens, num_parts;
   void* ws;
-  bool stream_kv;
+  bool stream_kv, fp8_kv;
 };
 
-template <class E, int D, int G, bool NT>
+template <class E, class KV, int D, int G, bool NT>
 int launch_mfma(const Args& a, hipStream_t st) {
   if (a.part_tokens > 0) {
     const int hpw = heads_per_workgroup(a.num_kv_heads);
     const long long grid = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
     if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     float* ws = static_cast<float*>(a.ws);
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<E, D, G, NT>), dim3((unsigned)grid), dim3(64 * hpw), 0, st,
+    hipLaunchKernelGGL((pa_decode_mfma_kernel<E, KV, D, G, NT>), dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                        a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                       a.num_blocks, a.qk_scale, a.part_tokens, a.num_parts, hpw, ws);
+                       a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, hpw, ws);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
                        a.out, ws, a.sl, a.num_heads, a.max_blocks, a.part_tokens, a.num_parts);
@@ -142,9 +181,9 @@ int launch_mfma(const Args& a, hipStream_t st) {
   int4* ws_seq = static_cast<int4*>(a.ws);
   float* ws_rec = reinterpret_cast<float*>(static_cast<char*>(a.ws) + balanced_seq_bytes(a.num_seqs));
   const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
-  hipLaunchKernelGGL((pa_decode_sk_kernel<E, D, G, NT>), dim3((unsigned)(groups * nwg)), dim3(64 * hpw), lds, st,
+  hipLaunchKernelGGL((pa_decode_sk_kernel<E, KV, D, G, NT>), dim3((unsigned)(groups * nwg)), dim3(64 * hpw), lds, st,
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks,
-                     a.num_blocks, a.qk_scale, hpw, nwg, ws_seq, ws_rec);
+                     a.num_blocks, a.qk_scale, a.v_scale, hpw, nwg, ws_seq, ws_rec);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   hipLaunchKernelGGL((pa_sk_merge_kernel<E, D, G>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
                      a.out, ws_seq, ws_rec, a.num_heads, hpw, nwg);
@@ -172,8 +211,10 @@ template <class E, int D, int G>
 int launch(const Args& a, hipStream_t st) {
   if constexpr (E::kBytes == 4) {
     return launch_valu<E, D, G>(a, st);
+  } else if (a.fp8_kv) {
+    return a.stream_kv ? launch_mfma<E, KvFp8, D, G, true>(a, st) : launch_mfma<E, KvFp8, D, G, false>(a, st);
   } else {
-    return a.stream_kv ? launch_mfma<E, D, G, true>(a, st) : launch_mfma<E, D, G, false>(a, st);
+    return a.stream_kv ? launch_mfma<E, Kv16, D, G, true>(a, st) : launch_mfma<E, Kv16, D, G, false>(a, st);
   }
 }
 
@@ -221,13 +262,14 @@ extern "C" size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head
   return pa::split_workspace_bytes(num_seqs, num_heads, head_size, np);
 }
 
-extern "C" int paged_attention_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
-                                      const int32_t* block_tables, const int32_t* seq_lens,
-                                      int num_seqs, int num_heads, int num_kv_heads, int head_size,
-                                      int block_size, int max_blocks_per_seq, int num_blocks,
-                                      int max_seq_len, float scale, int dtype, int partition_size,
-                                      unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace pa;
+namespace pa {
+namespace {
+
+int decode_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* seq_lens, int num_seqs, int num_heads,
+                int num_kv_heads, int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                int max_seq_len, float scale, int dtype, int partition_size, unsigned flags, void* workspace,
+                size_t workspace_bytes, void* stream, bool fp8_kv, float k_scale, float v_scale) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 ||
       max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0 || partition_size < 0)
     return PA_ERR_INVALID_ARG;
@@ -243,7 +285,8 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return PA_ERR_INVALID_ARG;
-  if ((long long)kBlockSize * num_kv_heads * head_size * elem_bytes(dtype) > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  const int kv_bytes = fp8_kv ? 1 : elem_bytes(dtype);
+  if ((long long)kBlockSize * num_kv_heads * head_size * kv_bytes > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
 
   Args a{};
   a.out = out; a.query = query;
@@ -251,7 +294,9 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   a.bt = block_tables; a.sl = seq_lens;
   a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks;
-  a.qk_scale = (float)((double)scale * 1.4426950408889634);
+  a.qk_scale = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  a.v_scale = v_scale;
+  a.fp8_kv = fp8_kv;
   a.part_tokens = 0; a.num_parts = 1;
   a.stream_kv = (flags & PA_FLAG_SHARED_BLOCKS) == 0;
   size_t need = 0;
@@ -275,6 +320,75 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
     case PA_F16: return dispatch_head<ElemF16>(a, head_size, group, st);
     default: return dispatch_head<ElemBF16>(a, head_size, group, st);
   }
+}
+
+bool positive_finite(float x) { return x > 0.f && x <= 3.4028234663852886e38f; }
+
+template <class E>
+void launch_scatter_fp8(const void* key, const void* value, void* k_cache, void* v_cache, const int32_t* slots,
+                        int num_tokens, int row_chunks, int64_t num_slots, float inv_k, float inv_v,
+                        hipStream_t st) {
+  const int threads = row_chunks >= 256 ? 256 : (row_chunks + 63) / 64 * 64;
+  const dim3 grid((unsigned)num_tokens, (unsigned)((row_chunks + threads - 1) / threads));
+  hipLaunchKernelGGL(pa_cache_scatter_fp8_kernel<E>, grid, dim3(threads), 0, st, static_cast<const char*>(key),
+                     static_cast<const char*>(value), static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache),
+                     slots, row_chunks, num_slots, inv_k, inv_v);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int paged_attention_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      int max_seq_len, float scale, int dtype, int partition_size,
+                                      unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype == PA_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  return pa::decode_impl(out, query, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                         head_size, block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale, dtype,
+                         partition_size, flags, workspace, workspace_bytes, stream, false, 1.0f, 1.0f);
+}
+
+extern "C" int paged_attention_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_tables, const int32_t* seq_lens,
+                                          int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                          int block_size, int max_blocks_per_seq, int num_blocks,
+                                          int max_seq_len, float scale, float k_scale, float v_scale, int dtype,
+                                          int partition_size, unsigned flags, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F16 && dtype != PA_BF16) return dtype == PA_F32 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+  if (!pa::positive_finite(k_scale) || !pa::positive_finite(v_scale)) return PA_ERR_INVALID_ARG;
+  return pa::decode_impl(out, query, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                         head_size, block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale, dtype,
+                         partition_size, flags, workspace, workspace_bytes, stream, true, k_scale, v_scale);
+}
+
+extern "C" int reshape_and_cache_fp8(const void* key, const void* value, void* k_cache, void* v_cache,
+                                     const int32_t* slot_mapping, int num_tokens, int num_kv_heads, int head_size,
+                                     int block_size, int num_blocks, int dtype, float k_scale, float v_scale,
+                                     void* stream) {
+  using namespace pa;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (!positive_finite(k_scale) || !positive_finite(v_scale)) return PA_ERR_INVALID_ARG;
+  const long long row_elems = (long long)num_kv_heads * head_size;
+  if (row_elems % 16 != 0 || row_elems / 16 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PA_ERR_INVALID_ARG;
+  const float inv_k = (float)(1.0 / (double)k_scale), inv_v = (float)(1.0 / (double)v_scale);
+  const int chunks = (int)(row_elems / 16);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case PA_F32: launch_scatter_fp8<ElemF32>(key, value, k_cache, v_cache, slot_mapping, num_tokens, chunks, num_slots, inv_k, inv_v, st); break;
+    case PA_F16: launch_scatter_fp8<ElemF16>(key, value, k_cache, v_cache, slot_mapping, num_tokens, chunks, num_slots, inv_k, inv_v, st); break;
+    default: launch_scatter_fp8<ElemBF16>(key, value, k_cache, v_cache, slot_mapping, num_tokens, chunks, num_slots, inv_k, inv_v, st); break;
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
@@ -308,7 +422,7 @@ extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
   using namespace pa;
   if (num_pairs < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
     return PA_ERR_INVALID_ARG;
-  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16 && dtype != PA_FP8_E4M3) return PA_ERR_INVALID_ARG;
   const long long block_bytes = (long long)block_size * num_kv_heads * head_size * elem_bytes(dtype);
   if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
   if (block_bytes / 16 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;

@@ -304,3 +304,22 @@ def unshare_prefix(wl: Workload, prefix_blocks: int) -> Workload:
 def random_rows(seed: int, stream: int, shape, dtype: str) -> torch.Tensor:
     """N(0, 1) tensor of ``shape`` in ``dtype`` from its own seeded stream."""
     return _normal(np.random.default_rng(np.random.SeedSequence([291, 200, seed, stream])), shape, dtype)
+
+
+def random_fp8_codes(seed: int, shape, poison_mask=None) -> torch.Tensor:
+    """uint8 OCP e4m3 codes drawn uniformly from the finite ones (every code
+    except 0x7F and 0xFF); where ``poison_mask`` is true, the NaN code 0x7F."""
+    rng = np.random.default_rng(np.random.SeedSequence([291, 400, seed]))
+    codes = rng.integers(0, 0x7F, size=shape, dtype=np.uint8) | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+    if poison_mask is not None:
+        codes[np.asarray(poison_mask)] = 0x7F
+    return torch.from_numpy(codes)
+
+
+def with_fp8_pools(wl: Workload, seed: int):
+    """The workload's tables, lengths and query with fp8 code pools of the
+    same shape: random finite codes where the 16-bit pools hold data, the NaN
+    code where they hold the NaN poison.  Returns (k_codes, v_codes)."""
+    km = torch.isnan(wl.k_cache.float()).numpy()
+    vm = torch.isnan(wl.v_cache.float()).numpy()
+    return random_fp8_codes(2 * seed, km.shape, km), random_fp8_codes(2 * seed + 1, vm.shape, vm)

@@ -110,6 +110,23 @@ def test_copy_blocks_host_errors():
     assert c(Hkv=1, D=1, BS=1, dtype=1) == -2                     # 2-byte blocks: not 16-byte chunks
 
 
+def test_fp8_host_errors():
+    lib = P.load_library()
+    d = lambda dtype=2, ks=0.5, vs=0.5, **kw: lib.paged_attention_decode_fp8(
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 16, 8, 64, 0, 0.1, ks, vs, dtype, 0, 0, None, 0, None)
+    assert d(dtype=0) == -2                                       # fp32 queries over fp8 pools: not built
+    assert d(dtype=3) == -1 and d(dtype=7) == -1
+    assert d(ks=0.0) == -1 and d(vs=-1.0) == -1 and d(ks=float("inf")) == -1 and d(vs=float("nan")) == -1
+    assert d() == -3                                              # balanced split needs its workspace
+    assert lib.paged_attention_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 16, 8, 64, 0, 0.1, 3, 0, 0,
+                                      None, 0, None) == -1        # fp8 is not a query type
+    r = lambda dtype=2, ks=0.5, vs=0.5, Hkv=8, D=128, n=4, key=FAKE: lib.reshape_and_cache_fp8(
+        key, FAKE, FAKE, FAKE, FAKE, n, Hkv, D, 16, 64, dtype, ks, vs, None)
+    assert r(n=0) == 0
+    assert r(key=None) == -1 and r(dtype=3) == -1 and r(ks=0.0) == -1
+    assert r(Hkv=1, D=8) == -2                                    # rows must be whole 16-code chunks
+
+
 def test_python_binding_refuses_host_tensors():
     q = torch.zeros(2, 4, 64)
     kc = torch.zeros(3, 16, 4, 64)

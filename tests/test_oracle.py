@@ -506,3 +506,99 @@ def test_planted_missing_last_token_is_caught(monkeypatch):
     monkeypatch.setattr(pa, "gather_rows",
                         lambda c, t, L, h: orig(c, t, max(int(L) - 1, 1) if int(L) > 1 else L, h))
     assert not _p1_ok() and not _p4_ok()
+
+
+# ---------------------------------------------------------------- fp8 (OCP E4M3) pools
+
+def test_e4m3_values_fixed_by_the_format():
+    # fixed points of the OCP E4M3 encoding: bias 7, subnormals m/8 * 2^-6, no infinities, S.1111.111 = NaN
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0, 0x39: 1.125,
+            0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in want.items():
+        assert oracle.e4m3_value(c) == v, hex(c)
+    assert np.signbit(oracle.e4m3_value(0x80)) and oracle.e4m3_value(0x80) == 0.0
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+    pos = [oracle.e4m3_value(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))                 # codes 0..0x7E increase
+    assert [oracle.e4m3_value(c | 0x80) for c in range(0x7F)] == [-v for v in pos]
+    assert np.array_equal(oracle.decode_values(np.arange(256, dtype=np.uint8), "e4m3")[:0x7F], pos)
+
+
+def test_e4m3_values_are_exact_in_bf16_and_f16():
+    v = oracle.E4M3_VALUES[~np.isnan(oracle.E4M3_VALUES)]
+    t = torch.from_numpy(v)
+    assert torch.equal(t.to(torch.bfloat16).double(), t)
+    assert torch.equal(t.to(torch.float16).double(), t)
+
+
+def test_e4m3_quantize_round_trip_and_ties():
+    finite = [c for c in range(256) if not np.isnan(oracle.E4M3_VALUES[c])]
+    vals = oracle.E4M3_VALUES[finite]
+    assert oracle.quantize_e4m3_ref(vals, 1.0).tolist() == finite          # every value maps to its own code
+    for sgn in (0, 0x80):
+        for c in range(0x7E):                                              # midpoints go to the even code
+            a, b = oracle.e4m3_value(c | sgn), oracle.e4m3_value((c + 1) | sgn)
+            mid = (a + b) / 2
+            got = int(oracle.quantize_e4m3_ref(np.array([mid]), 1.0)[0])
+            assert got == ((c | sgn) if c % 2 == 0 else ((c + 1) | sgn)), (hex(c), mid)
+            lo, hi = np.nextafter(np.float32(mid), np.float32(-np.inf)), np.nextafter(np.float32(mid), np.float32(np.inf))
+            near_a, near_b = (lo, hi) if a < b else (hi, lo)
+            assert int(oracle.quantize_e4m3_ref(np.array([near_a]), 1.0)[0]) == c | sgn
+            assert int(oracle.quantize_e4m3_ref(np.array([near_b]), 1.0)[0]) == (c + 1) | sgn
+
+
+def test_e4m3_quantize_saturation_nan_and_scale():
+    q = lambda xs, s=1.0: oracle.quantize_e4m3_ref(np.array(xs, dtype=np.float64), s).tolist()
+    assert q([448.0, 449.0, 500.0, 1e30, np.inf]) == [0x7E] * 5
+    assert q([-448.0, -1e30, -np.inf]) == [0xFE] * 3
+    assert np.isnan(oracle.E4M3_VALUES[q([np.nan])[0]])
+    assert q([2.0 ** -10, -2.0 ** -10, 1e-30, -1e-30]) == [0x00, 0x80, 0x00, 0x80]   # ties to +-0 (even)
+    assert q([3.0], 2.0) == q([1.5])                                   # x / scale
+    assert q([1.0], 0.1) == q([np.float32(1.0) * np.float32(1.0 / 0.1)])   # float32 product with 1/scale
+    assert q([10.0], 0.1)[0] == 0x6C              # 100 is halfway between 96 (0x6C) and 104 (0x6D): even code
+
+
+def test_fp8_decode_ref_is_the_scaled_dense_definition():
+    rng = np.random.default_rng(8)
+    S, Hq, Hkv, D, BS = 3, 4, 2, 16, 4
+    lens = [5, 9, 1]
+    nb = 8
+    kc = rng.integers(0, 0x7F, size=(nb, BS, Hkv, D)).astype(np.uint8) | (rng.integers(0, 2, size=(nb, BS, Hkv, D)) * 0x80).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, size=(nb, BS, Hkv, D)).astype(np.uint8)
+    bt = np.array([[3, 1, -1], [0, 5, 7], [6, -1, -1]], np.int32)
+    q = W.raw_numpy(torch.from_numpy(rng.standard_normal((S, Hq, D)).astype(np.float32)).to(torch.bfloat16))
+    ks, vs = 0.02, 0.03
+    got = oracle.paged_decode_ref(q, kc, vc, bt, np.array(lens, np.int32), 0.25, "bf16", kv_dtype="e4m3",
+                                  k_scale=ks, v_scale=vs)
+    for s in range(S):
+        for h in range(Hq):
+            kvh = h // (Hq // Hkv)
+            rows = [(bt[s, t // BS], t % BS) for t in range(lens[s])]
+            K = np.array([[oracle.e4m3_value(int(kc[b, o, kvh, d])) * ks for d in range(D)] for b, o in rows])
+            V = np.array([[oracle.e4m3_value(int(vc[b, o, kvh, d])) * vs for d in range(D)] for b, o in rows])
+            qv = oracle.decode_values(q[s, h], "bf16")
+            z = 0.25 * (K @ qv)
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            assert np.allclose(got[s, h], p @ V, rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_scatter_ref_quantizes_then_scatters():
+    rng = np.random.default_rng(9)
+    key = W.raw_numpy(torch.from_numpy(rng.standard_normal((5, 2, 16)).astype(np.float32) * 3).to(torch.bfloat16))
+    value = W.raw_numpy(torch.from_numpy(rng.standard_normal((5, 2, 16)).astype(np.float32)).to(torch.bfloat16))
+    kc = np.full((4, 4, 2, 16), 0x7F, np.uint8)
+    vc = kc.copy()
+    slots = np.array([3, 0, -1, 15, 6], np.int32)
+    gk, gv = oracle.reshape_and_cache_fp8_ref(key, value, kc, vc, slots, "bf16", 0.05, 0.01)
+    for i, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        b, o = divmod(int(sl), 4)
+        kv = oracle.decode_values(key[i], "bf16")
+        for h in range(2):
+            for d in range(16):
+                assert gk[b, o, h, d] == oracle.quantize_e4m3_ref(np.array([kv[h, d]]), 0.05)[0]
+    written = np.zeros(16, bool)
+    written[slots[slots >= 0]] = True
+    assert (gk.reshape(16, -1)[~written] == 0x7F).all()
