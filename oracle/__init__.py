@@ -28,6 +28,7 @@ from .paged_attention import (  # noqa: F401
     E4M3_VALUES,
     quantize_e4m3_ref,
     reshape_and_cache_fp8_ref,
+    paged_prefill_ref,
 )
 from .block_manager import (  # noqa: F401
     BlockManagerRef,

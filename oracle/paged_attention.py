@@ -323,3 +323,42 @@ def reshape_and_cache_fp8_ref(key, value, k_cache, v_cache, slot_mapping, dtype:
     kq = quantize_e4m3_ref(decode_values(key, dtype), k_scale)
     vq = quantize_e4m3_ref(decode_values(value, dtype), v_scale)
     return reshape_and_cache_ref(kq, vq, k_cache, v_cache, slot_mapping)
+
+
+def paged_prefill_ref(query, k_cache, v_cache, block_tables, seq_lens, query_start, scale: float, dtype: str,
+                      seqs=None, kv_dtype: str | None = None, k_scale: float = 1.0,
+                      v_scale: float = 1.0) -> np.ndarray:
+    """Several new tokens per sequence attending over the paged cache, causally.
+
+    yangyitao.com vLLM book preface (overview figure and its list): prefill,
+    decode and speculative decoding are one operation, giving a request N new
+    tokens; is96.com essay: chunked prefill cuts a long prompt into pieces
+    processed step by step.  Reading: the ``n = query_start[s+1] -
+    query_start[s]`` query rows of sequence s (packed in ``query[T, Hq, D]``)
+    are its last n tokens, whose K/V are already in the cache, so row i sits at
+    position ``p = seq_lens[s] - n + i`` and attends to tokens ``0 .. p``
+    (causal; decode is ``n = 1``).  Returns float64 ``[T, Hq, D]`` (rows of
+    sequences outside ``seqs`` stay zero).
+    """
+    T, Hq, D = query.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    S = len(seq_lens)
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape) or len(query_start) != S + 1:
+        raise ValueError("shape mismatch")
+    kvt = kv_dtype or dtype
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in (range(S) if seqs is None else seqs):
+        a, b, L = int(query_start[s]), int(query_start[s + 1]), int(seq_lens[s])
+        n = b - a
+        if n > L:
+            raise ValueError("a sequence has more query rows than tokens")
+        for kvh in range(Hkv):
+            K = decode_values(gather_rows(k_cache, block_tables[s], L, kvh), kvt) * k_scale
+            V = decode_values(gather_rows(v_cache, block_tables[s], L, kvh), kvt) * v_scale
+            for i in range(n):
+                p = L - n + i
+                q = decode_values(query[a + i], dtype)
+                for h in range(Hq):
+                    if kv_head_of(h, Hq, Hkv) == kvh:
+                        out[a + i, h], _ = softmax_attention(q[h], K[:p + 1], V[:p + 1], scale)
+    return out

@@ -602,3 +602,95 @@ def test_fp8_scatter_ref_quantizes_then_scatters():
     written = np.zeros(16, bool)
     written[slots[slots >= 0]] = True
     assert (gk.reshape(16, -1)[~written] == 0x7F).all()
+
+
+# ---------------------------------------------------------------- multi-token queries (causal)
+
+def _prefill_case(seed, lens, nq, Hq, Hkv, D, dtype="bf16"):
+    wl = W.make_random(seed, len(lens), Hq, Hkv, D, dtype, lens)
+    starts = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = W.random_rows(seed, 77, (int(starts[-1]), Hq, D), dtype)
+    return wl, starts, W.raw_numpy(q)
+
+
+def test_prefill_with_one_row_is_decode():
+    wl = W.make_random(41, 4, 8, 2, 32, "bf16", [1, 7, 40, 100])
+    q = W.raw_numpy(wl.query)
+    starts = np.arange(5, dtype=np.int32)
+    _, kc, vc, bt, sl = raw(wl)
+    a = oracle.paged_prefill_ref(q, kc, vc, bt, sl, starts, wl.scale, "bf16")
+    b = oracle.paged_decode_ref(q, kc, vc, bt, sl, wl.scale, "bf16")
+    assert np.array_equal(a, b)
+
+
+def test_prefill_row_is_decode_over_the_prefix():
+    """Row i of sequence s equals one-token decode over the sequence cut after position L - n + i."""
+    lens, nq = [9, 33, 20], [4, 33, 1]
+    wl, starts, q = _prefill_case(42, lens, nq, 8, 4, 16)
+    _, kc, vc, bt, sl = raw(wl)
+    got = oracle.paged_prefill_ref(q, kc, vc, bt, sl, starts, wl.scale, "bf16")
+    for s in range(3):
+        for i in range(nq[s]):
+            row = starts[s] + i
+            cut = np.array([lens[s] - nq[s] + i + 1], np.int32)
+            want = oracle.paged_decode_ref(q[row:row + 1], kc, vc, bt[s:s + 1], cut, wl.scale, "bf16")
+            assert np.array_equal(got[row], want[0])
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_prefill_equals_masked_dense_sdpa(G):
+    """Identity table, whole sequence as queries: torch SDPA (float64) with a causal mask."""
+    Hkv, D, L, BS = 2, 16, 37, 16
+    Hq = Hkv * G
+    rng = np.random.default_rng(1)
+    nb = -(-L // BS)
+    kc = rng.standard_normal((nb, BS, Hkv, D)).astype(np.float32)
+    vc = rng.standard_normal((nb, BS, Hkv, D)).astype(np.float32)
+    bt = np.arange(nb, dtype=np.int32)[None]
+    q = rng.standard_normal((L, Hq, D)).astype(np.float32)
+    got = oracle.paged_prefill_ref(q, kc, vc, bt, np.array([L], np.int32), np.array([0, L], np.int32), 0.3, "f32")
+    K = torch.from_numpy(kc.reshape(-1, Hkv, D)[:L].astype(np.float64)).permute(1, 0, 2)
+    V = torch.from_numpy(vc.reshape(-1, Hkv, D)[:L].astype(np.float64)).permute(1, 0, 2)
+    Q = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)
+    K, V = K.repeat_interleave(G, 0), V.repeat_interleave(G, 0)
+    want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=0.3)
+    assert np.allclose(got, want.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_brute_force_tiny():
+    lens, nq = [5, 3], [3, 2]
+    wl, starts, q = _prefill_case(44, lens, nq, 2, 1, 4, "f32")
+    _, kc, vc, bt, sl = raw(wl)
+    got = oracle.paged_prefill_ref(q, kc, vc, bt, sl, starts, 0.5, "f32")
+    bs = kc.shape[1]
+    for s in range(2):
+        for i in range(nq[s]):
+            p = lens[s] - nq[s] + i
+            for h in range(2):
+                qv = [float(x) for x in q[starts[s] + i, h]]
+                rows = [(int(bt[s, t // bs]), t % bs) for t in range(p + 1)]
+                z = [0.5 * math.fsum(qv[d] * float(kc[b, o, 0, d]) for d in range(4)) for b, o in rows]
+                m = max(z)
+                w = [math.exp(x - m) for x in z]
+                tot = math.fsum(w)
+                for d in range(4):
+                    v = math.fsum(w[j] * float(vc[b, o, 0, d]) for j, (b, o) in enumerate(rows)) / tot
+                    assert abs(got[starts[s] + i, h, d] - v) < 1e-12
+
+
+def test_prefill_planted_mistakes_fail():
+    lens, nq = [12], [5]
+    wl, starts, q = _prefill_case(45, lens, nq, 4, 2, 8)
+    _, kc, vc, bt, sl = raw(wl)
+    good = oracle.paged_prefill_ref(q, kc, vc, bt, sl, starts, wl.scale, "bf16")
+    # strict mask (a token does not see itself) and top-left alignment both change the rows
+    K = [oracle.decode_values(oracle.gather_rows(kc, bt[0], 12, h), "bf16") for h in range(2)]
+    V = [oracle.decode_values(oracle.gather_rows(vc, bt[0], 12, h), "bf16") for h in range(2)]
+    for shift in (-1, -(12 - 5)):
+        bad = np.array(good)
+        for i in range(5):
+            p = 12 - 5 + i + shift
+            for h in range(4):
+                qv = oracle.decode_values(q[i, h], "bf16")
+                bad[i, h], _ = oracle.softmax_attention(qv, K[h // 2][:max(p, 0) + 1], V[h // 2][:max(p, 0) + 1], wl.scale)
+        assert not np.allclose(bad, good)
