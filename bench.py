@@ -44,7 +44,10 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "block_manager"])
+    ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "block_manager", "prefill"])
+    ap.add_argument("--prefill-case", default="verify", choices=["verify", "chunk"],
+                    help="prefill: verify = the 8B batch with 4 query tokens per sequence (speculative "
+                         "verification); chunk = 8 sequences, 3584 cached + 512 new tokens")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="fp8: the same workload over OCP e4m3 pools (random finite codes, scales 1/128 and 1/96)")
     ap.add_argument("--steps", type=int, default=200)
@@ -257,6 +260,96 @@ def bench_copy_blocks(args):
     return rec
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args):
+    """Multi-token causal queries: speculative verification (memory-bound) or
+    a chunked prefill (matrix-core bound)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_291_amd as P
+    from paged_kv_cache_291_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    if args.prefill_case == "verify":
+        wl = W.make_config(3, args.seed, poison=False)
+        nq = np.full(wl.num_seqs, 4, dtype=np.int32)
+        desc = "speculative verification on the 8B-shaped GQA batch: 256 seqs, 4 query tokens each (32/8 heads, D=128, bf16)"
+    else:
+        S, L, n = 8, 4096, 512
+        wl = W.make_random(args.seed, S, 32, 8, 128, "bf16", [L] * S, poison=False)
+        nq = np.full(S, n, dtype=np.int32)
+        desc = "chunked prefill: 8 seqs x (3584 cached + 512 new tokens), 32/8 heads, D=128, bf16"
+    starts = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    T = int(starts[-1])
+    q = W.random_rows(args.seed, 500, (T, wl.num_heads, wl.head_size), wl.dtype).to(dev)
+    kc, vc = wl.k_cache.to(dev), wl.v_cache.to(dev)
+    bt, sl = torch.from_numpy(wl.block_tables).to(dev), torch.from_numpy(wl.seq_lens).to(dev)
+    qs = torch.from_numpy(starts).to(dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    mq = int(nq.max())
+
+    def step():
+        P.paged_attention_prefill(out, q, kc, vc, bt, sl, qs, wl.scale, max_query_len=mq, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K = args.steps
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(K):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K
+    launch = ev0.elapsed_time(ev1) / K / 1e3
+    D, Hq = wl.head_size, wl.num_heads
+    # (query row, visible key) pairs: row i of n sees L - n + i + 1 keys
+    pairs = int(sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2 for n, L in zip(nq, wl.seq_lens)))
+    flops = 4.0 * D * Hq * pairs
+    kv = wl.kv_bytes()
+    rec = {
+        "metric": "paged multi-token causal attention: " + ("KV GB/s" if args.prefill_case == "verify" else "TFLOP/s"),
+        "value": round(kv / wall / 1e9, 2) if args.prefill_case == "verify" else round(flops / wall / 1e12, 2),
+        "unit": "GB/s" if args.prefill_case == "verify" else "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": desc, "query_tokens": T, "kv_bytes": kv, "flops": flops},
+        "roofline": ({"bound": "hbm", "achieved": round(kv / launch / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(kv / launch / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                      "kernel": "pa_prefill_kernel", "bytes_per_launch": kv}
+                     if args.prefill_case == "verify" else
+                     {"bound": "mfma", "achieved": round(flops / launch / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(flops / launch / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "traffic": None, "kernel": "pa_prefill_kernel", "flops_per_launch": flops}),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        qr, kr, vr = W.raw_numpy(q.cpu()), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache)
+        done, el, work = 0, 0.0, 0.0
+        with threadpool_limits(1):
+            while done < wl.num_seqs and (el < min(args.cpu_seconds, 20.0) or done == 0):
+                t1 = time.perf_counter()
+                oracle.paged_prefill_ref(qr, kr, vr, wl.block_tables, wl.seq_lens, starts, wl.scale, wl.dtype,
+                                         seqs=[done])
+                el += time.perf_counter() - t1
+                n_, L_ = int(nq[done]), int(wl.seq_lens[done])
+                work += (L_ * wl.num_kv_heads * D * 2 * 2 if args.prefill_case == "verify"
+                         else 4.0 * D * Hq * (n_ * (L_ - n_) + n_ * (n_ + 1) // 2))
+                done += 1
+        rec["cpu_baseline"] = {"value": round(work / el / (1e9 if args.prefill_case == "verify" else 1e12), 5),
+                               "unit": rec["unit"], "cores": 1, "kind": "oracle",
+                               "sample": f"first {done} of {wl.num_seqs} sequences, float64 NumPy, {el:.2f} s"}
+    return rec
+
+
 def bench_block_manager(args):
     """Host block manager building decode steps of a 256-sequence batch."""
     import numpy as np
@@ -361,6 +454,9 @@ def main():
     P.load_library()
     if args.op == "copy_blocks":
         print(json.dumps(bench_copy_blocks(args)))
+        return
+    if args.op == "prefill":
+        print(json.dumps(bench_prefill(args)))
         return
     cfg = args.config
     ps = DEFAULT_PARTITION[cfg] if args.partition < 0 else args.partition

@@ -129,6 +129,48 @@ int paged_attention_decode(void* out, const void* query, const void* k_cache, co
                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Several new tokens per sequence, attending causally over the paged cache
+ * (chunked prefill and speculative verification; yangyitao.com vLLM book
+ * preface, overview list: prefill, decode and speculative decoding all give a
+ * request N new tokens; is96.com essay: chunked prefill processes a long
+ * prompt in pieces).
+ *
+ * Sequence s brings n_s = query_start[s+1] - query_start[s] query rows,
+ * query[query_start[s] + i] for i < n_s: its last n_s tokens, whose K/V are
+ * already in the pools (reshape_and_cache first).  Row i sits at position
+ * p = seq_lens[s] - n_s + i and attends to tokens 0 .. p:
+ *
+ *   out[query_start[s] + i, h, :] = sum_{t <= p} softmax_t(scale <q, K_t>) V_t
+ *
+ * with K_t, V_t read through the block table as in paged_attention_decode
+ * (kv head h / (num_heads / num_kv_heads)).  n_s == 1 is decode.
+ *
+ *  out, query     [num_query_tokens, num_heads, head_size] (dtype: PA_F16 or
+ *                 PA_BF16; PA_F32 gives PA_ERR_UNSUPPORTED)
+ *  query_start    int32 [num_seqs + 1], non-decreasing, query_start[0] = 0,
+ *                 query_start[num_seqs] = num_query_tokens
+ *  max_query_len  >= every n_s (sizes the grid); 0 means num_query_tokens
+ *  other arguments as in paged_attention_decode; no workspace.
+ * Rows of a sequence with n_s > seq_lens[s], a length past its table row or a
+ * block id outside the pool are NaN.  Rows beyond max_query_len are not
+ * written.
+ */
+int paged_attention_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
+                            int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads, int head_size,
+                            int block_size, int max_blocks_per_seq, int num_blocks, int max_query_len,
+                            float scale, int dtype, unsigned flags, void* stream);
+
+/* paged_attention_prefill over fp8 (e4m3) pools with one scale per pool
+ * (see paged_attention_decode_fp8). */
+int paged_attention_prefill_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
+                                int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
+                                int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                                int max_query_len, float scale, float k_scale, float v_scale, int dtype,
+                                unsigned flags, void* stream);
+
+/*
  * Scatter new tokens' K/V rows into their cache slots (csdn article,
  * section 4 point 3: gather-scatter in place of contiguous access; section 2
  * part 4: a new token joins its sequence's blocks).

@@ -2,7 +2,7 @@
 
 Entry points (same names as the C ABI in ``include/pagedattn.h``):
 ``paged_attention_decode``, ``reshape_and_cache``, ``paged_attention_decode_fp8``,
-``reshape_and_cache_fp8``, ``copy_blocks``,
+``reshape_and_cache_fp8``, ``paged_attention_prefill``, ``copy_blocks``,
 ``pa_decode_workspace_size``, ``pa_status_string``, and ``BlockManager``
 over the host block manager (``pa_bm_*``).  Inputs of the device calls are
 torch tensors on a HIP device; torch provides memory and streams only.
@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     pa_status_string,
     paged_attention_decode,
     paged_attention_decode_fp8,
+    paged_attention_prefill,
     reshape_and_cache,
     reshape_and_cache_fp8,
 )

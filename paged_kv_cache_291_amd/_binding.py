@@ -26,7 +26,8 @@ DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache",
-            "paged_attention_decode_fp8", "reshape_and_cache_fp8",
+            "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
+            "paged_attention_prefill_fp8",
             "copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_allocate", "pa_bm_append_slots", "pa_bm_fork",
             "pa_bm_append_batch", "pa_bm_free", "pa_bm_num_free_blocks", "pa_bm_free_list", "pa_bm_ref_count", "pa_bm_seq_len",
             "pa_bm_block_tables", "pa_bm_num_copies", "pa_bm_take_copies")
@@ -68,6 +69,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.reshape_and_cache_fp8.restype = c_int
     lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                           c_float, vp]
+    lib.paged_attention_prefill.restype = c_int
+    lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [c_int] * 9 + [c_float, c_int,
+                                                                                         ctypes.c_uint, vp]
+    lib.paged_attention_prefill_fp8.restype = c_int
+    lib.paged_attention_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [c_int] * 9 + [
+        c_float, c_float, c_float, c_int, ctypes.c_uint, vp]
     lib.copy_blocks.restype = c_int
     lib.copy_blocks.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
     pbm = ctypes.POINTER(vp)
@@ -256,6 +263,42 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch
         _fp8_pool(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int32), T, Hkv, D, BS, NB,
         DTYPE_CODES[key.dtype], float(k_scale), float(v_scale), _stream(stream))
     _check(rc)
+
+
+def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                            query_start: torch.Tensor, scale: float, max_query_len: int = 0,
+                            k_scale: Optional[float] = None, v_scale: Optional[float] = None, flags: int = 0,
+                            stream=None) -> torch.Tensor:
+    """Several query rows per sequence (its last tokens), causal over the
+    paged cache.  query/out ``[T, Hq, D]`` bf16/fp16, query_start int32
+    ``[S + 1]``.  With ``k_scale``/``v_scale`` the pools hold e4m3 codes."""
+    T, Hq, D = query.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    S = seq_lens.shape[0]
+    if tuple(out.shape) != (T, Hq, D) or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between out/query/k_cache/v_cache")
+    if query.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {query.dtype}")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or query_start.shape != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and query_start [S + 1]")
+    dt = query.dtype
+    fp8 = k_scale is not None or v_scale is not None
+    common = (_dev(out, "out", dt), _dev(query, "query", dt),
+              _fp8_pool(k_cache, "k_cache") if fp8 else _dev(k_cache, "k_cache", dt),
+              _fp8_pool(v_cache, "v_cache") if fp8 else _dev(v_cache, "v_cache", dt),
+              _dev(block_tables, "block_tables", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+              _dev(query_start, "query_start", torch.int32), S, T, Hq, Hkv, D, BS, block_tables.shape[1], NB,
+              int(max_query_len), float(scale))
+    lib = load_library()
+    if fp8:
+        rc = lib.paged_attention_prefill_fp8(*common, float(k_scale if k_scale is not None else 1.0),
+                                             float(v_scale if v_scale is not None else 1.0), DTYPE_CODES[dt],
+                                             int(flags), _stream(stream))
+    else:
+        rc = lib.paged_attention_prefill(*common, DTYPE_CODES[dt], int(flags), _stream(stream))
+    _check(rc)
+    return out
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,

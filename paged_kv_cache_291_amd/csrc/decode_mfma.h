@@ -262,6 +262,105 @@ __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __res
   return false;
 }
 
+// Causal variant for multi-token queries: the 16 rows of the tile are
+// (token, head) pairs with their own last visible position `row_last` (one
+// per lane: this lane's row l%16), all blocks [0, b_end) of the sequence are
+// streamed, and blocks from `mask_from` on are masked per row.  V rows past
+// the sequence's last token `seq_last` are zeroed (they may hold anything);
+// inside the sequence a masked key only needs its zero probability.  Every
+// row sees key 0, so every row's running max is finite after block 0.
+template <class E, class KV, int D, bool NT>
+__device__ __forceinline__ bool mfma_segment_causal(MfmaState<D>& st, const char* __restrict__ k_cache,
+                                                    const char* __restrict__ v_cache,
+                                                    const int* __restrict__ bt_row, int b_end, int mask_from,
+                                                    int row_last, int seq_last, int num_blocks, int num_kv_heads,
+                                                    int kvh, float qk_scale, int lane) {
+  using SH = MfmaShape<D>;
+  using M = Mfma<E>;
+  using IO = KvIo<KV, E, D>;
+  using Blk = typename IO::Blk;
+  constexpr int BS = kBlockSize, KS = SH::kKs, VE = SH::kVe, VW = SH::kVw;
+  const int g = lane >> 4;
+  const int blk_bytes = BS * num_kv_heads * IO::kRowBytes;
+  const int row_stride = num_kv_heads * IO::kRowBytes;
+  const int k_off = IO::k_off(lane & 15, g, num_kv_heads, kvh);
+  const int v_off = IO::v_off(lane & 15, g, num_kv_heads, kvh);
+
+  auto load_block = [&](int phys, Blk& b) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(k_cache + (int64_t)phys * blk_bytes, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(v_cache + (int64_t)phys * blk_bytes, blk_bytes);
+    IO::template load<NT>(rk, rv, k_off, v_off, row_stride, b);
+  };
+
+  // key0: position of the block's first key
+  auto consume = [&](const Blk& b, int key0, bool masked) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) sc = M::qk(IO::k_operand(b, k), st.qb[k], sc);
+    // lane l holds S[row = l%16][key = key0 + 4*(l/16) + i]; row_last is that row's limit
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = sc[i] * qk_scale;
+      if (masked && key0 + 4 * g + i > row_last) z[i] = -INFINITY;
+    }
+    const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
+      const float m_new = fmaxf(st.m_ref, bm);
+      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first block
+      st.l_part *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int T = 0; T < VE; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[T][i] *= ar[i];
+      st.m_ref = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - st.m_ref);
+    st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
+    const u32x2 pa = {pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
+    uint32_t v[4][VW];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < VW; ++q) v[j][q] = (masked && key0 + 4 * g + j > seq_last) ? 0u : IO::v_word(b, j, q);
+#pragma unroll
+    for (int T = 0; T < VE; ++T) {
+      const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2 vb = {__builtin_amdgcn_perm(v[1][T >> 1], v[0][T >> 1], sel),
+                        __builtin_amdgcn_perm(v[3][T >> 1], v[2][T >> 1], sel)};
+      st.acc[T] = M::pv(pa, vb, st.acc[T]);
+    }
+  };
+
+  for (int cb = 0; cb < b_end; cb += 64) {
+    const int n = min(64, b_end - cb);
+    const int id = lane < n ? bt_row[cb + lane] : 0;
+    if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) return true;
+    Blk A, B;
+    load_block(__builtin_amdgcn_readlane(id, 0), A);
+    int j = 0;
+    for (; j + 2 < n; j += 2) {
+      load_block(__builtin_amdgcn_readlane(id, j + 1), B);
+      consume(A, (cb + j) * BS, cb + j >= mask_from);
+      load_block(__builtin_amdgcn_readlane(id, j + 2), A);
+      consume(B, (cb + j + 1) * BS, cb + j + 1 >= mask_from);
+    }
+    if (j + 1 < n) {
+      load_block(__builtin_amdgcn_readlane(id, j + 1), B);
+      consume(A, (cb + j) * BS, cb + j >= mask_from);
+      consume(B, (cb + j + 1) * BS, cb + j + 1 >= mask_from);
+    } else {
+      consume(A, (cb + j) * BS, cb + j >= mask_from);
+    }
+  }
+  return false;
+}
+
 // Normalise and write the G heads of the segment: to `out` rows
 // out_row0 + h (rec == nullptr), or as partial records rec + h * rec_stride.
 template <class E, int D, int G>
@@ -459,6 +558,71 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     mfma_finish<E, D, G>(st, bad, out, row0, rec, REC, v_scale, lane);
     u += b1 - b0;
     ++s;
+  }
+}
+
+// ---- multi-token queries (chunked prefill, speculative verification)
+
+// Grid (ceil(max_tiles / 4), num_seqs, num_kv_heads); 4 waves, wave w owns
+// query tile 4*blockIdx.x + w of the sequence: rows r = 0..15 are (token
+// tile*16/G + r/G, query head kvh*G + r%G).  Tiles past the sequence's query
+// rows exit.  Token i of the n query rows sits at position L - n + i and sees
+// positions 0 .. L - n + i.  Out-of-contract lengths (n > L, L past the table
+// row) or block ids give NaN rows.
+template <class E, class KV, int D, int G, bool NT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const char* __restrict__ k_cache,
+                  const char* __restrict__ v_cache, const int* __restrict__ block_tables,
+                  const int* __restrict__ seq_lens, const int* __restrict__ query_start, int num_heads,
+                  int num_kv_heads, int max_blocks, int num_blocks, float qk_scale, float v_scale) {
+  using SH = MfmaShape<D>;
+  using IO = KvIo<KV, ElemBF16, D>;
+  constexpr int BS = kBlockSize, TPT = 16 / G, VE = SH::kVe;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x * 4 + wave, s = blockIdx.y, kvh = blockIdx.z;
+  const int q0 = query_start[s], n = query_start[s + 1] - q0, L = seq_lens[s];
+  const int tok0 = tile * TPT;
+  if (n <= 0 || tok0 >= n) return;
+  const bool bad_len = n > L || (int64_t)L > (int64_t)max_blocks * BS;
+  const int g = lane >> 4, c = lane & 15;
+
+  // this lane's row c: token tok0 + c/G (padding rows past n reuse the last token's limit)
+  const int my_tok = tok0 + c / G;
+  const bool row_live = my_tok < n;
+  MfmaState<D> st;
+  {
+    const char* qrow = static_cast<const char*>(query) +
+                       ((int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G) * SH::kRow;
+#pragma unroll
+    for (int k = 0; k < SH::kKs; ++k)
+      st.qb[k] = row_live ? *reinterpret_cast<const u32x4*>(qrow + 2 * IO::q_elem(g, k)) : u32x4{0u, 0u, 0u, 0u};
+    st.m_ref = -INFINITY;
+    st.l_part = 0.f;
+#pragma unroll
+    for (int T = 0; T < VE; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool bad = bad_len;
+  if (!bad_len) {
+    const int first_pos = L - n + tok0;                          // the tile's smallest limit
+    const int last_pos = L - n + min(tok0 + TPT, n) - 1;          // and largest
+    const int row_last = L - n + min(my_tok, n - 1);
+    bad = mfma_segment_causal<E, KV, D, NT>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+                                            last_pos / BS + 1, (first_pos + 1) / BS, row_last, L - 1, num_blocks,
+                                            num_kv_heads, kvh, qk_scale, lane);
+  }
+  // rows r = 4*(l/16) + i of the accumulator: token tok0 + r/G, head r%G
+  const float l_row = rows_sum(st.l_part);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    const float lr = __shfl(l_row, r);
+    const int tok = tok0 + r / G;
+    if (tok >= n) continue;
+    const float inv = lr > 0.f ? v_scale / lr : 0.f;
+    float o[VE];
+#pragma unroll
+    for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
+    store_run<E, VE>(out, ((int64_t)(q0 + tok) * num_heads + kvh * G + r % G) * D + VE * c, o);
   }
 }
 

@@ -324,6 +324,71 @@ int decode_impl(void* out, const void* query, const void* k_cache, const void* v
 
 bool positive_finite(float x) { return x > 0.f && x <= 3.4028234663852886e38f; }
 
+template <class E, class KV, int D, int G>
+int launch_prefill(void* out, const void* query, const void* kc, const void* vc, const int32_t* bt,
+                   const int32_t* sl, const int32_t* qs, int num_seqs, int num_heads, int num_kv_heads,
+                   int max_blocks, int num_blocks, int max_query_len, float qk_scale, float v_scale, bool nt,
+                   hipStream_t st) {
+  const int tiles = ceil_div(max_query_len * G, 16);
+  const dim3 grid((unsigned)ceil_div(tiles, 4), (unsigned)num_seqs, (unsigned)num_kv_heads);
+  auto k = nt ? pa_prefill_kernel<E, KV, D, G, true> : pa_prefill_kernel<E, KV, D, G, false>;
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, st, out, query, static_cast<const char*>(kc),
+                     static_cast<const char*>(vc), bt, sl, qs, num_heads, num_kv_heads, max_blocks, num_blocks,
+                     qk_scale, v_scale);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+template <class E, class KV, int D>
+int prefill_group(int group, void* out, const void* query, const void* kc, const void* vc, const int32_t* bt,
+                  const int32_t* sl, const int32_t* qs, int S, int Hq, int Hkv, int MB, int NB, int mq, float qks,
+                  float vs, bool nt, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_prefill<E, KV, D, 1>(out, query, kc, vc, bt, sl, qs, S, Hq, Hkv, MB, NB, mq, qks, vs, nt, st);
+    case 2: return launch_prefill<E, KV, D, 2>(out, query, kc, vc, bt, sl, qs, S, Hq, Hkv, MB, NB, mq, qks, vs, nt, st);
+    case 4: return launch_prefill<E, KV, D, 4>(out, query, kc, vc, bt, sl, qs, S, Hq, Hkv, MB, NB, mq, qks, vs, nt, st);
+    case 8: return launch_prefill<E, KV, D, 8>(out, query, kc, vc, bt, sl, qs, S, Hq, Hkv, MB, NB, mq, qks, vs, nt, st);
+    default: return PA_ERR_UNSUPPORTED;
+  }
+}
+
+int prefill_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start, int num_seqs,
+                 int num_query_tokens, int num_heads, int num_kv_heads, int head_size, int block_size,
+                 int max_blocks_per_seq, int num_blocks, int max_query_len, float scale, int dtype, unsigned flags,
+                 void* stream, bool fp8_kv, float k_scale, float v_scale) {
+  if (num_seqs < 0 || num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0 || max_query_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+  if (flags & ~(unsigned)PA_FLAG_SHARED_BLOCKS) return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (head_size != 64 && head_size != 128) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  const int group = num_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PA_ERR_INVALID_ARG;
+  const int kv_bytes = fp8_kv ? 1 : elem_bytes(dtype);
+  if ((long long)kBlockSize * num_kv_heads * head_size * kv_bytes > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  const int mq = max_query_len > 0 ? max_query_len : num_query_tokens;
+  const float qks = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  const bool nt = (flags & PA_FLAG_SHARED_BLOCKS) == 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define PA_PREFILL(E, KV, D) prefill_group<E, KV, D>(group, out, query, k_cache, v_cache, block_tables, seq_lens, \
+    query_start, num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_blocks, mq, qks, v_scale, nt, st)
+  if (dtype == PA_F16) {
+    if (fp8_kv) return head_size == 64 ? PA_PREFILL(ElemF16, KvFp8, 64) : PA_PREFILL(ElemF16, KvFp8, 128);
+    return head_size == 64 ? PA_PREFILL(ElemF16, Kv16, 64) : PA_PREFILL(ElemF16, Kv16, 128);
+  }
+  if (fp8_kv) return head_size == 64 ? PA_PREFILL(ElemBF16, KvFp8, 64) : PA_PREFILL(ElemBF16, KvFp8, 128);
+  return head_size == 64 ? PA_PREFILL(ElemBF16, Kv16, 64) : PA_PREFILL(ElemBF16, Kv16, 128);
+#undef PA_PREFILL
+}
+
 template <class E>
 void launch_scatter_fp8(const void* key, const void* value, void* k_cache, void* v_cache, const int32_t* slots,
                         int num_tokens, int row_chunks, int64_t num_slots, float inv_k, float inv_v,
@@ -435,4 +500,27 @@ extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
   hipLaunchKernelGGL(pa_copy_blocks_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<u32x4*>(k_cache), static_cast<u32x4*>(v_cache), src, dst, chunks, num_blocks);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" int paged_attention_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       const int32_t* query_start, int num_seqs, int num_query_tokens,
+                                       int num_heads, int num_kv_heads, int head_size, int block_size,
+                                       int max_blocks_per_seq, int num_blocks, int max_query_len, float scale,
+                                       int dtype, unsigned flags, void* stream) {
+  return pa::prefill_impl(out, query, k_cache, v_cache, block_tables, seq_lens, query_start, num_seqs,
+                          num_query_tokens, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                          num_blocks, max_query_len, scale, dtype, flags, stream, false, 1.0f, 1.0f);
+}
+
+extern "C" int paged_attention_prefill_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables, const int32_t* seq_lens,
+                                           const int32_t* query_start, int num_seqs, int num_query_tokens,
+                                           int num_heads, int num_kv_heads, int head_size, int block_size,
+                                           int max_blocks_per_seq, int num_blocks, int max_query_len, float scale,
+                                           float k_scale, float v_scale, int dtype, unsigned flags, void* stream) {
+  if (!pa::positive_finite(k_scale) || !pa::positive_finite(v_scale)) return PA_ERR_INVALID_ARG;
+  return pa::prefill_impl(out, query, k_cache, v_cache, block_tables, seq_lens, query_start, num_seqs,
+                          num_query_tokens, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                          num_blocks, max_query_len, scale, dtype, flags, stream, true, k_scale, v_scale);
 }

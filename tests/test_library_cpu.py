@@ -127,6 +127,18 @@ def test_fp8_host_errors():
     assert r(Hkv=1, D=8) == -2                                    # rows must be whole 16-code chunks
 
 
+def test_prefill_host_errors():
+    lib = P.load_library()
+    f = lambda dtype=2, S=4, T=8, D=128, BS=16, Hq=8, Hkv=2, mq=0, qs=FAKE, ptr=FAKE: lib.paged_attention_prefill(
+        ptr, FAKE, FAKE, FAKE, FAKE, FAKE, qs, S, T, Hq, Hkv, D, BS, 8, 64, mq, 0.1, dtype, 0, None)
+    assert f(S=0) == 0 and f(T=0) == 0                            # nothing to do
+    assert f(dtype=0) == -2 and f(dtype=3) == -1                  # fp32 not built; fp8 is not a query type
+    assert f(qs=None) == -1 and f(ptr=None) == -1 and f(mq=-1) == -1
+    assert f(D=96) == -2 and f(BS=32) == -2 and f(Hq=12, Hkv=8) == -1
+    assert lib.paged_attention_prefill_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, 2, 128, 16, 8, 64, 0,
+                                           0.1, 0.0, 1.0, 2, 0, None) == -1   # scale must be positive
+
+
 def test_python_binding_refuses_host_tensors():
     q = torch.zeros(2, 4, 64)
     kc = torch.zeros(3, 16, 4, 64)

@@ -1,0 +1,108 @@
+"""Multi-token causal queries over the paged cache on the GPU against the
+float64 oracle: edge lengths and query counts (n = 1 is decode, n = L is a
+whole prompt), every head size, group size and type, fp8 pools, contract
+violations, and a chunked-prefill batch at full size checked on sampled rows
+(each row equals decode over the sequence cut after its position)."""
+
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_291_amd as P
+from paged_kv_cache_291_amd import workloads as W
+from helpers import HALF_ULP, TOL
+
+pytestmark = pytest.mark.gpu
+
+LENS = [1, 2, 16, 17, 40, 64, 100, 300, 513, 33, 7, 600]
+NQ = [1, 2, 16, 5, 40, 3, 1, 33, 17, 0, 7, 64]
+
+
+def _case(seed, Hq, Hkv, D, dtype, lens=LENS, nq=NQ):
+    wl = W.make_random(seed, len(lens), Hq, Hkv, D, dtype, lens, extra_table_cols=1)
+    starts = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = W.random_rows(seed, 99, (int(starts[-1]), Hq, D), dtype)
+    return wl, starts, q
+
+
+def _gpu(wl, starts, q, kc=None, vc=None, fp8=None, max_q=0, bt=None, sl=None):
+    out = torch.empty_like(q, device="cuda")
+    kw = {} if fp8 is None else dict(k_scale=fp8[0], v_scale=fp8[1])
+    P.paged_attention_prefill(out, q.cuda(), (kc if kc is not None else wl.k_cache).cuda(),
+                              (vc if vc is not None else wl.v_cache).cuda(),
+                              torch.from_numpy(wl.block_tables if bt is None else bt).cuda(),
+                              torch.from_numpy(wl.seq_lens if sl is None else sl).cuda(),
+                              torch.from_numpy(starts).cuda(), wl.scale, max_query_len=max_q, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy()
+
+
+SWEEP = [(dt, D, Hq, Hkv) for dt in ("bf16", "f16") for D in (64, 128) for (Hq, Hkv) in ((4, 4), (4, 2), (8, 2), (16, 2))]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", SWEEP)
+def test_prefill_sweep(dtype, D, Hq, Hkv):
+    seed = zlib.crc32(f"prefill-{dtype}-{D}-{Hq}-{Hkv}".encode()) % 10000
+    wl, starts, q = _case(seed, Hq, Hkv, D, dtype)
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                   wl.block_tables, wl.seq_lens, starts, wl.scale, dtype)
+    for max_q in (0, max(NQ)):
+        g = _gpu(wl, starts, q, max_q=max_q)
+        diff = np.abs(g - ref)
+        print(f"prefill {dtype} D={D} {Hq}/{Hkv} max_q={max_q}: max-abs {diff.max():.3e}", flush=True)
+        assert np.isfinite(g).all()
+        assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8)])
+def test_prefill_fp8_pools(Hq, Hkv):
+    wl, starts, q = _case(600 + Hq, Hq, Hkv, 128, "bf16")
+    kc8, vc8 = W.with_fp8_pools(wl, 61)
+    ks, vs = 1.0 / 128, 1.0 / 96
+    g = _gpu(wl, starts, q, kc8, vc8, fp8=(ks, vs))
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), kc8.numpy(), vc8.numpy(), wl.block_tables, wl.seq_lens, starts,
+                                   wl.scale, "bf16", kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    diff = np.abs(g - ref)
+    print(f"prefill fp8 {Hq}/{Hkv}: max-abs {diff.max():.3e}", flush=True)
+    assert np.isfinite(g).all()
+    assert float(np.max(diff - (TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref)))) <= 0.0
+
+
+def test_prefill_contract_violations_give_nan_rows():
+    lens, nq = [40, 20, 30, 50], [3, 4, 2, 5]
+    wl, starts, q = _case(71, 8, 2, 64, "bf16", lens, nq)
+    bt, sl = wl.block_tables.copy(), wl.seq_lens.copy()
+    sl[1] = 3                                             # fewer tokens than query rows
+    sl[2] = bt.shape[1] * 16 + 1                          # past the table row
+    bt[3, 1] = wl.num_blocks                              # id outside the pool
+    g = _gpu(wl, starts, q, bt=bt, sl=sl)
+    for s in (1, 2, 3):
+        assert np.isnan(g[starts[s]:starts[s + 1]]).all(), s
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                   wl.block_tables, wl.seq_lens, starts, wl.scale, "bf16", seqs=[0])
+    assert np.max(np.abs(g[:3] - ref[:3])) <= TOL["bf16"] + HALF_ULP["bf16"] * np.max(np.abs(ref[:3]))
+
+
+def test_chunked_prefill_batch_full_size():
+    """8 sequences of 4096 tokens whose last 512 are the query chunk (8B head shape)."""
+    S, L, n, Hq, Hkv, D = 8, 4096, 512, 32, 8, 128
+    wl, starts, q = _case(72, Hq, Hkv, D, "bf16", [L] * S, [n] * S)
+    g = _gpu(wl, starts, q)
+    assert np.isfinite(g).all()
+    kc, vc, qr = W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache), W.raw_numpy(q)
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for s in range(S):
+        for i in sorted({0, n - 1, *rng.choice(n, 4, replace=False).tolist()}):
+            row = starts[s] + i
+            cut = np.array([L - n + i + 1], np.int32)
+            want = oracle.paged_decode_ref(qr[row:row + 1], kc, vc, wl.block_tables[s:s + 1], cut, wl.scale, "bf16")
+            d = np.abs(g[row] - want[0])
+            worst = max(worst, float(d.max()))
+            assert np.all(d <= TOL["bf16"] + HALF_ULP["bf16"] * np.abs(want[0])), (s, i)
+    print(f"chunked prefill 8 x (3584 + 512): max-abs {worst:.3e} on sampled rows", flush=True)
