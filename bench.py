@@ -326,7 +326,7 @@ def bench_prefill(args):
                      if args.prefill_case == "verify" else
                      {"bound": "mfma", "achieved": round(flops / launch / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(flops / launch / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                      "traffic": None, "kernel": "pa_prefill_kernel", "flops_per_launch": flops}),
+                      "traffic": None, "kernel": "pa_prefill_lds_kernel", "flops_per_launch": flops}),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

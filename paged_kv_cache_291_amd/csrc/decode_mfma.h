@@ -626,4 +626,208 @@ pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const 
   }
 }
 
+// ---- multi-token queries, K/V shared through LDS
+
+// Blocks per LDS stage and the padded row pitch (bytes) of a 16-bit K/V row
+// in LDS: 16 extra bytes shift consecutive rows by four banks, so the 16
+// lanes reading one MFMA operand (16 rows, same column) hit different banks.
+constexpr int kPfStageBlocks = 4;
+template <int D> constexpr int pf_row_pitch() { return D * 2 + 16; }
+template <int D> constexpr int pf_stage_bytes() { return kPfStageBlocks * 2 * kBlockSize * pf_row_pitch<D>(); }
+
+// Grid: one workgroup of 8 waves per (sequence, kv head, 8 consecutive query
+// tiles); wave w owns tile 8*grp + w (16 (token, head) rows as in
+// pa_prefill_kernel).  The workgroup streams the sequence's blocks in stages
+// of kPfStageBlocks: all 512 threads copy a stage's K and V rows of this kv
+// head into LDS (double-buffered, one barrier per stage; fp8 codes are
+// widened to the query type on the way; rows past the sequence end are
+// zero), then every wave consumes the stage's blocks it can see.  Each K/V
+// byte is read from memory once per 8 tiles instead of once per tile.
+// The linear workgroup id is split so that all workgroups of one (sequence,
+// kv head) land on the same XCD (workgroups are dealt to the 8 XCDs round
+// robin), where its K/V stay in that XCD's L2.
+template <class E, class KV, int D, int G, bool NT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, const char* __restrict__ k_cache,
+                      const char* __restrict__ v_cache, const int* __restrict__ block_tables,
+                      const int* __restrict__ seq_lens, const int* __restrict__ query_start, int num_seqs,
+                      int num_heads, int num_kv_heads, int max_blocks, int num_blocks, int groups_per_pair,
+                      float qk_scale, float v_scale) {
+  using SH = MfmaShape<D>;
+  using M = Mfma<E>;
+  using IO = KvIo<Kv16, ElemBF16, D>;                 // the query map of 16-bit K rows (LDS holds 16-bit rows)
+  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe, VW = SH::kVw;
+  constexpr int RP = pf_row_pitch<D>();
+  constexpr int KVB = KV::kBytes;                     // bytes per element in the pools
+  constexpr int CPR = D * KVB / 16;                   // 16-byte chunks per pool row
+  constexpr int CHUNKS = kPfStageBlocks * 2 * BS * CPR;
+  constexpr int PER_T = CHUNKS / 512;                 // chunks per thread and stage
+  static_assert(CHUNKS % 512 == 0, "stage must split evenly over the workgroup");
+  __shared__ __align__(16) char smem[2 * pf_stage_bytes<D>()];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int pair = (slot / groups_per_pair) * 8 + xcd, grp = slot % groups_per_pair;
+  if (pair >= num_seqs * num_kv_heads) return;
+  const int s = pair / num_kv_heads, kvh = pair - s * num_kv_heads;
+  const int q0 = query_start[s], n = query_start[s + 1] - q0, L = seq_lens[s];
+  const int wg_tok0 = grp * 8 * TPT;
+  if (n <= 0 || wg_tok0 >= n) return;                // the whole workgroup: uniform
+  const bool bad_len = n > L || (int64_t)L > (int64_t)max_blocks * BS;
+
+  const int g = lane >> 4, c = lane & 15;
+  const int tok0 = wg_tok0 + wave * TPT;
+  const bool active = tok0 < n && !bad_len;
+  const int my_tok = tok0 + c / G;
+  const bool row_live = my_tok < n;
+  MfmaState<D> st;
+  {
+    const char* qrow = static_cast<const char*>(query) +
+                       ((int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G) * SH::kRow;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      st.qb[k] = row_live ? *reinterpret_cast<const u32x4*>(qrow + 2 * IO::q_elem(g, k)) : u32x4{0u, 0u, 0u, 0u};
+    st.m_ref = -INFINITY;
+    st.l_part = 0.f;
+#pragma unroll
+    for (int T = 0; T < VE; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int my_first = L - n + tok0, my_last = L - n + min(tok0 + TPT, n) - 1;
+  const int my_b_end = active ? my_last / BS + 1 : 0;
+  const int my_mask_from = (my_first + 1) / BS;
+  const int row_last = L - n + min(my_tok, n - 1);
+  const int wg_last = L - n + min(wg_tok0 + 8 * TPT, n) - 1;
+  const int wg_b_end = bad_len ? 0 : wg_last / BS + 1;
+  const int* bt_row = block_tables + (int64_t)s * max_blocks;
+  const int blk_bytes = BS * num_kv_heads * D * KVB;
+
+  // one stage: PER_T chunks per thread, chunk q -> (block, K|V, row, column)
+  u32x4 regs[PER_T];
+  bool bad_id = false;
+  auto issue = [&](int stage) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int q = tid + 512 * i;
+      const int col = q % CPR, row = (q / CPR) % BS, kv = (q / (CPR * BS)) & 1, blk = q / (CPR * BS * 2);
+      const int bi = stage * kPfStageBlocks + blk;
+      const int tok = bi * BS + row;
+      regs[i] = u32x4{0u, 0u, 0u, 0u};
+      if (bi < wg_b_end && tok < L) {
+        const int id = bt_row[bi];
+        if ((unsigned)id < (unsigned)num_blocks) {
+          const char* base = (kv ? v_cache : k_cache) + (int64_t)id * blk_bytes + (row * num_kv_heads + kvh) * D * KVB;
+          regs[i] = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + col)
+                       : reinterpret_cast<const u32x4*>(base)[col];
+        } else {
+          bad_id = true;
+        }
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+    char* sb = smem + buf * pf_stage_bytes<D>();
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int q = tid + 512 * i;
+      const int col = q % CPR, row = (q / CPR) % BS, kv = (q / (CPR * BS)) & 1, blk = q / (CPR * BS * 2);
+      char* dst = sb + ((blk * 2 + kv) * BS + row) * RP;
+      if constexpr (KVB == 2) {
+        *reinterpret_cast<u32x4*>(dst + col * 16) = regs[i];
+      } else {                                        // 16 codes -> 16 elements of E
+        const u32x4 w = regs[i];
+        const u32x4 lo = {fp8x2_to<E, false>(w[0]), fp8x2_to<E, true>(w[0]), fp8x2_to<E, false>(w[1]),
+                          fp8x2_to<E, true>(w[1])};
+        const u32x4 hi = {fp8x2_to<E, false>(w[2]), fp8x2_to<E, true>(w[2]), fp8x2_to<E, false>(w[3]),
+                          fp8x2_to<E, true>(w[3])};
+        *reinterpret_cast<u32x4*>(dst + col * 32) = lo;
+        *reinterpret_cast<u32x4*>(dst + col * 32 + 16) = hi;
+      }
+    }
+  };
+  auto consume = [&](const char* kb, const char* vb, int key0, bool masked) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      sc = M::qk(*reinterpret_cast<const u32x4*>(kb + c * RP + 64 * k + 16 * g), st.qb[k], sc);
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = sc[i] * qk_scale;
+      if (masked && key0 + 4 * g + i > row_last) z[i] = -INFINITY;
+    }
+    const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
+      const float m_new = fmaxf(st.m_ref, bm);
+      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+      st.l_part *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int T = 0; T < VE; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[T][i] *= ar[i];
+      st.m_ref = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - st.m_ref);
+    st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
+    const u32x2 pa = {pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
+    uint32_t v[4][VW];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const char* vr = vb + (4 * g + j) * RP + VE * 2 * c;
+      if constexpr (VW == 4) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(vr);
+        v[j][0] = t[0]; v[j][1] = t[1]; v[j][2] = t[2]; v[j][3] = t[3];
+      } else {
+        const u32x2 t = *reinterpret_cast<const u32x2*>(vr);
+        v[j][0] = t[0]; v[j][1] = t[1];
+      }
+    }
+#pragma unroll
+    for (int T = 0; T < VE; ++T) {
+      const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2 vb2 = {__builtin_amdgcn_perm(v[1][T >> 1], v[0][T >> 1], sel),
+                         __builtin_amdgcn_perm(v[3][T >> 1], v[2][T >> 1], sel)};
+      st.acc[T] = M::pv(pa, vb2, st.acc[T]);
+    }
+  };
+
+  const int stages = (wg_b_end + kPfStageBlocks - 1) / kPfStageBlocks;
+  if (stages > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+  for (int stg = 0; stg < stages; ++stg) {
+    if (stg + 1 < stages) issue(stg + 1);
+    const char* sb = smem + (stg & 1) * pf_stage_bytes<D>();
+#pragma unroll 1
+    for (int j = 0; j < kPfStageBlocks; ++j) {
+      const int bi = stg * kPfStageBlocks + j;
+      if (bi >= my_b_end) break;
+      consume(sb + (j * 2) * BS * RP, sb + (j * 2 + 1) * BS * RP, bi * BS, bi >= my_mask_from);
+    }
+    if (stg + 1 < stages) commit((stg + 1) & 1);
+    __syncthreads();
+  }
+  const bool bad = bad_len || __syncthreads_or(bad_id);
+
+  const float l_row = rows_sum(st.l_part);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    const float lr = __shfl(l_row, r);
+    const int tok = tok0 + r / G;
+    if (tok >= n) continue;
+    const float inv = lr > 0.f ? v_scale / lr : 0.f;
+    float o[VE];
+#pragma unroll
+    for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
+    store_run<E, VE>(out, ((int64_t)(q0 + tok) * num_heads + kvh * G + r % G) * D + VE * c, o);
+  }
+}
+
 }  // namespace pa

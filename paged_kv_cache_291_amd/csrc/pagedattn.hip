@@ -31,6 +31,9 @@ namespace {
 constexpr int kSkWorkgroups = 256;
 // Largest batch the balanced split handles (its prefix sums live in LDS).
 constexpr int kSkMaxSeqs = 16383;
+// Multi-token queries: from this many 16-row query tiles per (sequence, kv
+// head) on, workgroups of 8 tiles share each K/V block through LDS.
+constexpr int kPrefillLdsTiles = 4;
 
 // ------------------------------------------------------------ scatter kernel
 
@@ -330,6 +333,18 @@ int launch_prefill(void* out, const void* query, const void* kc, const void* vc,
                    int max_blocks, int num_blocks, int max_query_len, float qk_scale, float v_scale, bool nt,
                    hipStream_t st) {
   const int tiles = ceil_div(max_query_len * G, 16);
+  if (tiles >= kPrefillLdsTiles) {
+    // many query tiles per (sequence, kv head): 8 tiles per workgroup share K/V through LDS
+    const int gpp = ceil_div(tiles, 8);
+    const long long pairs = (long long)num_seqs * num_kv_heads;
+    const long long grid = (pairs + 7) / 8 * 8 * gpp;
+    if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    auto k = nt ? pa_prefill_lds_kernel<E, KV, D, G, true> : pa_prefill_lds_kernel<E, KV, D, G, false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(512), 0, st, out, query, static_cast<const char*>(kc),
+                       static_cast<const char*>(vc), bt, sl, qs, num_seqs, num_heads, num_kv_heads, max_blocks,
+                       num_blocks, gpp, qk_scale, v_scale);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
   const dim3 grid((unsigned)ceil_div(tiles, 4), (unsigned)num_seqs, (unsigned)num_kv_heads);
   auto k = nt ? pa_prefill_kernel<E, KV, D, G, true> : pa_prefill_kernel<E, KV, D, G, false>;
   hipLaunchKernelGGL(k, grid, dim3(256), 0, st, out, query, static_cast<const char*>(kc),

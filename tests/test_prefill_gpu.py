@@ -106,3 +106,25 @@ def test_chunked_prefill_batch_full_size():
             worst = max(worst, float(d.max()))
             assert np.all(d <= TOL["bf16"] + HALF_ULP["bf16"] * np.abs(want[0])), (s, i)
     print(f"chunked prefill 8 x (3584 + 512): max-abs {worst:.3e} on sampled rows", flush=True)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 32, 8), ("f16", 64, 8, 8), ("bf16", 64, 16, 2)])
+def test_few_query_rows_per_sequence(dtype, D, Hq, Hkv, fp8):
+    """Speculative verification: a few rows per sequence, one tile per (sequence, kv head)."""
+    lens = [1, 3, 16, 17, 200, 513, 40, 2]
+    nq = [1, 3, 2, 3, 3, 1, 0, 2]
+    wl, starts, q = _case(80 + Hq + D, Hq, Hkv, D, dtype, lens, nq)
+    if fp8:
+        kc8, vc8 = W.with_fp8_pools(wl, 81)
+        g = _gpu(wl, starts, q, kc8, vc8, fp8=(1 / 128, 1 / 96), max_q=3)
+        ref = oracle.paged_prefill_ref(W.raw_numpy(q), kc8.numpy(), vc8.numpy(), wl.block_tables, wl.seq_lens,
+                                       starts, wl.scale, dtype, kv_dtype="e4m3", k_scale=1 / 128, v_scale=1 / 96)
+    else:
+        g = _gpu(wl, starts, q, max_q=3)
+        ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                       wl.block_tables, wl.seq_lens, starts, wl.scale, dtype)
+    diff = np.abs(g - ref)
+    print(f"verify-shaped {dtype} D={D} {Hq}/{Hkv} fp8={fp8}: max-abs {diff.max():.3e}", flush=True)
+    assert np.isfinite(g).all()
+    assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
