@@ -149,8 +149,17 @@ int paged_attention_decode(void* out, const void* query, const void* k_cache, co
  *                 PA_BF16; PA_F32 gives PA_ERR_UNSUPPORTED)
  *  query_start    int32 [num_seqs + 1], non-decreasing, query_start[0] = 0,
  *                 query_start[num_seqs] = num_query_tokens
- *  max_query_len  >= every n_s (sizes the grid); 0 means num_query_tokens
- *  other arguments as in paged_attention_decode; no workspace.
+ *  max_query_len  >= every n_s (sizes the grid and picks the path); 0 means
+ *                 num_query_tokens
+ *  workspace      device buffer of >= pa_prefill_workspace_size(...) bytes,
+ *                 256-byte aligned (NULL when that size is 0); scratch, as for
+ *                 paged_attention_decode
+ *  other arguments as in paged_attention_decode.
+ * When max_query_len * (num_heads / num_kv_heads) <= 16 (speculative
+ * verification: each kv head's query rows fit one 16-row tile) and num_seqs
+ * <= 16383, the batch's blocks are split evenly over the GPU as in decode and
+ * a second kernel merges partial results (needs the workspace); otherwise one
+ * wave per 16-row tile, 8 tiles sharing K/V through LDS when there are many.
  * Rows of a sequence with n_s > seq_lens[s], a length past its table row or a
  * block id outside the pool are NaN.  Rows beyond max_query_len are not
  * written.
@@ -159,7 +168,14 @@ int paged_attention_prefill(void* out, const void* query, const void* k_cache, c
                             const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
                             int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads, int head_size,
                             int block_size, int max_blocks_per_seq, int num_blocks, int max_query_len,
-                            float scale, int dtype, unsigned flags, void* stream);
+                            float scale, int dtype, unsigned flags, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes paged_attention_prefill(_fp8) needs with these sizes (0:
+ * none):  round_up(num_seqs * 16, 256) + 256 * num_kv_heads * 2 * 16 *
+ * (head_size + 4) * 4 on the split path, else 0.  0 for invalid sizes. */
+size_t pa_prefill_workspace_size(int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
+                                 int head_size, int max_query_len);
 
 /* paged_attention_prefill over fp8 (e4m3) pools with one scale per pool
  * (see paged_attention_decode_fp8). */
@@ -168,7 +184,7 @@ int paged_attention_prefill_fp8(void* out, const void* query, const void* k_cach
                                 int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
                                 int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
                                 int max_query_len, float scale, float k_scale, float v_scale, int dtype,
-                                unsigned flags, void* stream);
+                                unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Scatter new tokens' K/V rows into their cache slots (csdn article,

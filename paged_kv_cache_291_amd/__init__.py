@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     decode_workspace_bytes,
     load_library,
     pa_decode_workspace_size,
+    pa_prefill_workspace_size,
     pa_status_string,
     paged_attention_decode,
     paged_attention_decode_fp8,

@@ -27,7 +27,7 @@ FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache",
             "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
-            "paged_attention_prefill_fp8",
+            "paged_attention_prefill_fp8", "pa_prefill_workspace_size",
             "copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_allocate", "pa_bm_append_slots", "pa_bm_fork",
             "pa_bm_append_batch", "pa_bm_free", "pa_bm_num_free_blocks", "pa_bm_free_list", "pa_bm_ref_count", "pa_bm_seq_len",
             "pa_bm_block_tables", "pa_bm_num_copies", "pa_bm_take_copies")
@@ -70,11 +70,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                           c_float, vp]
     lib.paged_attention_prefill.restype = c_int
-    lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [c_int] * 9 + [c_float, c_int,
-                                                                                         ctypes.c_uint, vp]
+    lib.paged_attention_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [c_int] * 9 + [
+        c_float, c_int, ctypes.c_uint, vp, c_size, vp]
     lib.paged_attention_prefill_fp8.restype = c_int
     lib.paged_attention_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [c_int] * 9 + [
-        c_float, c_float, c_float, c_int, ctypes.c_uint, vp]
+        c_float, c_float, c_float, c_int, ctypes.c_uint, vp, c_size, vp]
+    lib.pa_prefill_workspace_size.restype = c_size
+    lib.pa_prefill_workspace_size.argtypes = [c_int] * 6
     lib.copy_blocks.restype = c_int
     lib.copy_blocks.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
     pbm = ctypes.POINTER(vp)
@@ -265,14 +267,21 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, k_cache: torch
     _check(rc)
 
 
+def pa_prefill_workspace_size(num_seqs: int, num_query_tokens: int, num_heads: int, num_kv_heads: int,
+                              head_size: int, max_query_len: int) -> int:
+    return int(load_library().pa_prefill_workspace_size(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                                        head_size, max_query_len))
+
+
 def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
                             v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                             query_start: torch.Tensor, scale: float, max_query_len: int = 0,
                             k_scale: Optional[float] = None, v_scale: Optional[float] = None, flags: int = 0,
-                            stream=None) -> torch.Tensor:
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Several query rows per sequence (its last tokens), causal over the
     paged cache.  query/out ``[T, Hq, D]`` bf16/fp16, query_start int32
-    ``[S + 1]``.  With ``k_scale``/``v_scale`` the pools hold e4m3 codes."""
+    ``[S + 1]``.  With ``k_scale``/``v_scale`` the pools hold e4m3 codes.
+    A workspace is allocated when the call needs one and none is given."""
     T, Hq, D = query.shape
     NB, BS, Hkv, Dk = k_cache.shape
     S = seq_lens.shape[0]
@@ -284,6 +293,12 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: tor
         raise ValueError("block_tables must be [S, max_blocks] and query_start [S + 1]")
     dt = query.dtype
     fp8 = k_scale is not None or v_scale is not None
+    ws_ptr, ws_bytes = 0, 0
+    need = pa_prefill_workspace_size(S, T, Hq, Hkv, D, int(max_query_len)) if S > 0 else 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     common = (_dev(out, "out", dt), _dev(query, "query", dt),
               _fp8_pool(k_cache, "k_cache") if fp8 else _dev(k_cache, "k_cache", dt),
               _fp8_pool(v_cache, "v_cache") if fp8 else _dev(v_cache, "v_cache", dt),
@@ -294,9 +309,9 @@ def paged_attention_prefill(out: torch.Tensor, query: torch.Tensor, k_cache: tor
     if fp8:
         rc = lib.paged_attention_prefill_fp8(*common, float(k_scale if k_scale is not None else 1.0),
                                              float(v_scale if v_scale is not None else 1.0), DTYPE_CODES[dt],
-                                             int(flags), _stream(stream))
+                                             int(flags), ws_ptr, ws_bytes, _stream(stream))
     else:
-        rc = lib.paged_attention_prefill(*common, DTYPE_CODES[dt], int(flags), _stream(stream))
+        rc = lib.paged_attention_prefill(*common, DTYPE_CODES[dt], int(flags), ws_ptr, ws_bytes, _stream(stream))
     _check(rc)
     return out
 

@@ -149,6 +149,22 @@ __device__ __forceinline__ void mfma_begin(MfmaState<D>& st, const void* query, 
   for (int T = 0; T < SH::kVe; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Start a segment whose 16 rows are arbitrary query rows: lane l loads row
+// q_row (its row l%16; zeros when !live) with the d map of KV.
+template <class KV, int D>
+__device__ __forceinline__ void mfma_begin_row(MfmaState<D>& st, const void* query, int64_t q_row, bool live, int g) {
+  using SH = MfmaShape<D>;
+  using IO = KvIo<KV, ElemBF16, D>;
+  const char* qrow = static_cast<const char*>(query) + q_row * SH::kRow;
+#pragma unroll
+  for (int k = 0; k < SH::kKs; ++k)
+    st.qb[k] = live ? *reinterpret_cast<const u32x4*>(qrow + 2 * IO::q_elem(g, k)) : u32x4{0u, 0u, 0u, 0u};
+  st.m_ref = -INFINITY;
+  st.l_part = 0.f;
+#pragma unroll
+  for (int T = 0; T < SH::kVe; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 // Blocks [b_begin, b_end) of one sequence for kv head `kvh`; tokens at or past
 // t_end are masked.  Returns true if a block id of the range is out of the
 // pool (the segment's result is then undefined and must be reported as NaN).
@@ -264,17 +280,20 @@ __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __res
 
 // Causal variant for multi-token queries: the 16 rows of the tile are
 // (token, head) pairs with their own last visible position `row_last` (one
-// per lane: this lane's row l%16), all blocks [0, b_end) of the sequence are
-// streamed, and blocks from `mask_from` on are masked per row.  V rows past
+// per lane: this lane's row l%16).  Blocks [b_begin, b_end) of the sequence
+// are streamed; blocks from `mask_from` on are masked per row.  V rows past
 // the sequence's last token `seq_last` are zeroed (they may hold anything);
-// inside the sequence a masked key only needs its zero probability.  Every
-// row sees key 0, so every row's running max is finite after block 0.
-template <class E, class KV, int D, bool NT>
-__device__ __forceinline__ bool mfma_segment_causal(MfmaState<D>& st, const char* __restrict__ k_cache,
-                                                    const char* __restrict__ v_cache,
-                                                    const int* __restrict__ bt_row, int b_end, int mask_from,
-                                                    int row_last, int seq_last, int num_blocks, int num_kv_heads,
-                                                    int kvh, float qk_scale, int lane) {
+// inside the sequence a masked key only needs its zero probability.  A row
+// may see no key of the whole range (a range holding only the sequence's
+// last keys): its max stays -inf and its probabilities and sum stay 0, so
+// a partial result of such a row weighs nothing in the merge.  LOCK as in
+// mfma_segment.
+template <class E, class KV, int D, bool NT, bool LOCK>
+__device__ __forceinline__ bool mfma_segment_rows(MfmaState<D>& st, const char* __restrict__ k_cache,
+                                                  const char* __restrict__ v_cache, const int* __restrict__ bt_row,
+                                                  int b_begin, int b_end, int mask_from, int row_last, int seq_last,
+                                                  int num_blocks, int num_kv_heads, int kvh, float qk_scale,
+                                                  int lane) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
   using IO = KvIo<KV, E, D>;
@@ -307,7 +326,8 @@ __device__ __forceinline__ bool mfma_segment_causal(MfmaState<D>& st, const char
     const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
     if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
       const float m_new = fmaxf(st.m_ref, bm);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first block
+      // 0 on a row's first visible block; a row with nothing visible yet keeps 0 state
+      const float alpha = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
       st.l_part *= alpha;
       float ar[4];
 #pragma unroll
@@ -320,7 +340,8 @@ __device__ __forceinline__ bool mfma_segment_causal(MfmaState<D>& st, const char
     }
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - st.m_ref);
+    for (int i = 0; i < 4; ++i)
+      p[i] = (masked && z[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[i] - st.m_ref);
     st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
     const u32x2 pa = {pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
     uint32_t v[4][VW];
@@ -337,28 +358,41 @@ __device__ __forceinline__ bool mfma_segment_causal(MfmaState<D>& st, const char
     }
   };
 
-  for (int cb = 0; cb < b_end; cb += 64) {
-    const int n = min(64, b_end - cb);
-    const int id = lane < n ? bt_row[cb + lane] : 0;
-    if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) return true;
-    Blk A, B;
-    load_block(__builtin_amdgcn_readlane(id, 0), A);
-    int j = 0;
-    for (; j + 2 < n; j += 2) {
-      load_block(__builtin_amdgcn_readlane(id, j + 1), B);
-      consume(A, (cb + j) * BS, cb + j >= mask_from);
-      load_block(__builtin_amdgcn_readlane(id, j + 2), A);
-      consume(B, (cb + j + 1) * BS, cb + j + 1 >= mask_from);
+  // Blocks before mask_from and from mask_from on run as two separate
+  // pipelines, each with the mask fixed at compile time: a branch between a
+  // load and its use would make every consume wait for all loads in flight.
+  auto run = [&](auto masked_tag, int lo, int hi) -> bool {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    for (int cb = lo; cb < hi; cb += 64) {
+      const int n = min(64, hi - cb);
+      const int id = lane < n ? bt_row[cb + lane] : 0;
+      if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) return true;
+      Blk A, B;
+      if constexpr (LOCK) __builtin_amdgcn_s_barrier();
+      load_block(__builtin_amdgcn_readlane(id, 0), A);
+      int j = 0;
+      for (; j + 2 < n; j += 2) {
+        if constexpr (LOCK) __builtin_amdgcn_s_barrier();
+        load_block(__builtin_amdgcn_readlane(id, j + 1), B);
+        consume(A, (cb + j) * BS, MASKED);
+        if constexpr (LOCK) __builtin_amdgcn_s_barrier();
+        load_block(__builtin_amdgcn_readlane(id, j + 2), A);
+        consume(B, (cb + j + 1) * BS, MASKED);
+      }
+      if (j + 1 < n) {
+        if constexpr (LOCK) __builtin_amdgcn_s_barrier();
+        load_block(__builtin_amdgcn_readlane(id, j + 1), B);
+        consume(A, (cb + j) * BS, MASKED);
+        consume(B, (cb + j + 1) * BS, MASKED);
+      } else {
+        consume(A, (cb + j) * BS, MASKED);
+      }
     }
-    if (j + 1 < n) {
-      load_block(__builtin_amdgcn_readlane(id, j + 1), B);
-      consume(A, (cb + j) * BS, cb + j >= mask_from);
-      consume(B, (cb + j + 1) * BS, cb + j + 1 >= mask_from);
-    } else {
-      consume(A, (cb + j) * BS, cb + j >= mask_from);
-    }
-  }
-  return false;
+    return false;
+  };
+  const int split = min(max(mask_from, b_begin), b_end);
+  if (run(std::false_type{}, b_begin, split)) return true;
+  return run(std::true_type{}, split, b_end);
 }
 
 // Normalise and write the G heads of the segment: to `out` rows
@@ -438,6 +472,41 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
                        (int64_t)num_parts * REC, v_scale, lane);
 }
 
+// Multi-token rows: accumulator row r = 4*(l/16) + i is (token r/G, head
+// r%G) of kv head kvh; rows of tokens >= nq are padding.  Whole rows go to
+// out[(q_tok0 + token) * num_heads + kvh*G + head]; partial rows to records
+// rec + r * rec_stride (16 per wave).
+template <class E, int D, int G>
+__device__ __forceinline__ void mfma_finish_rows(const MfmaState<D>& st, bool bad, void* __restrict__ out,
+                                                 int q_tok0, int nq, int num_heads, int kvh,
+                                                 float* __restrict__ rec, int64_t rec_stride, float out_scale,
+                                                 int lane) {
+  constexpr int VE = MfmaShape<D>::kVe;
+  const int g = lane >> 4, c = lane & 15;
+  const float l_head = rows_sum(st.l_part);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    const float lh = __shfl(l_head, r);
+    const float mh = __shfl(st.m_ref, r);
+    if (r / G >= nq) continue;
+    const float inv = lh > 0.f ? out_scale / lh : 0.f;
+    float o[VE];
+#pragma unroll
+    for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
+    if (rec == nullptr) {
+      store_run<E, VE>(out, ((int64_t)(q_tok0 + r / G) * num_heads + kvh * G + r % G) * D + VE * c, o);
+    } else {
+      float* rr = rec + r * rec_stride;
+      store_f32_run<VE>(rr + kRecHead + VE * c, o);
+      if (c == 0) {
+        rr[0] = bad ? qnan() : mh;
+        rr[1] = bad ? qnan() : lh;
+      }
+    }
+  }
+}
+
 // ---- balanced split (stream-K over the batch's blocks)
 
 // Range of flattened blocks of workgroup `rank` (of nwg) when U blocks are
@@ -486,7 +555,7 @@ __device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int n
 }
 
 // Grid: head_groups * nwg workgroups of hpw waves (kv heads hg*hpw + wave).
-// Dynamic LDS: (num_seqs + 1) ints.  ws_seq[s] (written by head group 0):
+// Dynamic LDS: (num_seqs + 1) ints, twice that with MQ.  ws_seq[s] (written by head group 0):
 // {w1, first block, end block, total blocks} where w1 is the range holding
 // the sequence's first block if the sequence runs past that range's end, -1
 // otherwise (written whole here, or no blocks).  ws_rec: partial records, 2
@@ -495,16 +564,21 @@ __device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int n
 // that have no blocks: zeros for length 0, NaN for an out-of-contract length.
 // A workgroup is up to 8 waves; 12 wave slots per CU would still hold only
 // one, so the register budget is that of 2 waves per SIMD.
-template <class E, class KV, int D, int G, bool NT>
+// MQ: several query tokens per sequence (query_start[s] .. query_start[s+1]),
+// at most 16 / G, so a wave's 16 rows are the (token, head) pairs of its kv
+// head; the sequence's final blocks are masked per row (causal), partial
+// records hold 16 rows per wave, and pa_sk_merge_mq_kernel merges them.
+template <class E, class KV, int D, int G, bool NT, bool MQ = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
                     const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                     const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                     int num_seqs, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
                     float qk_scale, float v_scale, int hpw, int nwg, int4* __restrict__ ws_seq,
-                    float* __restrict__ ws_rec) {
+                    float* __restrict__ ws_rec, const int* __restrict__ query_start = nullptr) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
+  constexpr int RPW = MQ ? 16 : G;             // record rows per wave and slot
   extern __shared__ int s_cum[];
   __shared__ int s_wsum[16];
 
@@ -513,6 +587,11 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int kvh = hg * hpw + wave;
 
   blocks_prefix_sum(seq_lens, num_seqs, max_blocks, s_cum, s_wsum);
+  int* s_qs = s_cum + num_seqs + 1;            // MQ: query_start staged in LDS
+  if constexpr (MQ) {
+    for (int i = tid; i <= num_seqs; i += blockDim.x) s_qs[i] = query_start[i];
+    __syncthreads();
+  }
   const int U = s_cum[num_seqs];
   const int u0 = sk_range_begin(rank, U, nwg), u1 = sk_range_begin(rank + 1, U, nwg);
   if (hg == 0 && u0 < u1) {
@@ -529,9 +608,17 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
   for (int s = rank; s < num_seqs; s += nwg) {
     if (s_cum[s + 1] != s_cum[s]) continue;
     if (hg == 0 && tid == 0) ws_seq[s] = int4{-1, 0, 0, U};
-    const float v = seq_lens[s] == 0 ? 0.f : qnan();
-    const int64_t e0 = ((int64_t)s * num_heads + kvh * G) * D;
-    for (int i = lane; i < G * D; i += 64) store_elem<E>(out, e0 + i, v);
+    if constexpr (MQ) {                        // query rows of a sequence without blocks break the contract
+      const int a = s_qs[s], nq = s_qs[s + 1] - a;
+      for (int t = 0; t < nq; ++t) {
+        const int64_t e0 = ((int64_t)(a + t) * num_heads + kvh * G) * D;
+        for (int i = lane; i < G * D; i += 64) store_elem<E>(out, e0 + i, qnan());
+      }
+    } else {
+      const float v = seq_lens[s] == 0 ? 0.f : qnan();
+      const int64_t e0 = ((int64_t)s * num_heads + kvh * G) * D;
+      for (int i = lane; i < G * D; i += 64) store_elem<E>(out, e0 + i, v);
+    }
   }
   if (u0 >= u1) return;
 
@@ -542,20 +629,39 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     if (s_cum[mid] <= u0) lo = mid; else hi = mid;
   }
   int s = lo;
-  float* rec_wg = ws_rec + ((int64_t)blockIdx.x * 2 * hpw + wave) * G * REC;
+  float* rec_wg = ws_rec + ((int64_t)blockIdx.x * 2 * hpw + wave) * RPW * REC;
   for (int u = u0; u < u1;) {
     const int c0 = s_cum[s], c1 = s_cum[s + 1];
     if (c1 == c0) { ++s; continue; }
     const int b0 = u - c0, b1 = min(c1, u1) - c0;
     const int L = seq_lens[s];
-    const int64_t row0 = (int64_t)s * num_heads + kvh * G;
-    MfmaState<D> st;
-    mfma_begin<KV, D, G>(st, query, row0, lane >> 4, lane & 15);
-    const bool bad = mfma_segment<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, b0, b1,
-                                            min(L, b1 * BS), num_blocks, num_kv_heads, kvh, qk_scale, lane);
     const bool whole = b0 == 0 && b1 == c1 - c0;
-    float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * G * REC);
-    mfma_finish<E, D, G>(st, bad, out, row0, rec, REC, v_scale, lane);
+    float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * RPW * REC);
+    if constexpr (MQ) {
+      const int a = s_qs[s], nq = s_qs[s + 1] - a;
+      if (nq > 0) {                            // same for every wave of the workgroup
+        const int g = lane >> 4, c = lane & 15;
+        const int tok = c / G;
+        const bool live = tok < nq;
+        MfmaState<D> st;
+        mfma_begin_row<KV, D>(st, query, (int64_t)(a + (live ? tok : 0)) * num_heads + kvh * G + c % G, live, g);
+        const int row_last = L - nq + min(tok, nq - 1);
+        bool bad = nq > L;
+        if (!bad)
+          bad = mfma_segment_rows<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+                                                      b0, b1, (L - nq + 1) / BS, row_last, L - 1, num_blocks,
+                                                      num_kv_heads, kvh, qk_scale, lane);
+        mfma_finish_rows<E, D, G>(st, bad, out, a, nq, num_heads, kvh, rec, REC, v_scale, lane);
+      }
+    } else {
+      const int64_t row0 = (int64_t)s * num_heads + kvh * G;
+      MfmaState<D> st;
+      mfma_begin<KV, D, G>(st, query, row0, lane >> 4, lane & 15);
+      const bool bad = mfma_segment<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+                                                        b0, b1, min(L, b1 * BS), num_blocks, num_kv_heads, kvh,
+                                                        qk_scale, lane);
+      mfma_finish<E, D, G>(st, bad, out, row0, rec, REC, v_scale, lane);
+    }
     u += b1 - b0;
     ++s;
   }
@@ -590,25 +696,15 @@ pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const 
   const int my_tok = tok0 + c / G;
   const bool row_live = my_tok < n;
   MfmaState<D> st;
-  {
-    const char* qrow = static_cast<const char*>(query) +
-                       ((int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G) * SH::kRow;
-#pragma unroll
-    for (int k = 0; k < SH::kKs; ++k)
-      st.qb[k] = row_live ? *reinterpret_cast<const u32x4*>(qrow + 2 * IO::q_elem(g, k)) : u32x4{0u, 0u, 0u, 0u};
-    st.m_ref = -INFINITY;
-    st.l_part = 0.f;
-#pragma unroll
-    for (int T = 0; T < VE; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  mfma_begin_row<KV, D>(st, query, (int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G, row_live, g);
   bool bad = bad_len;
   if (!bad_len) {
     const int first_pos = L - n + tok0;                          // the tile's smallest limit
     const int last_pos = L - n + min(tok0 + TPT, n) - 1;          // and largest
     const int row_last = L - n + min(my_tok, n - 1);
-    bad = mfma_segment_causal<E, KV, D, NT>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
-                                            last_pos / BS + 1, (first_pos + 1) / BS, row_last, L - 1, num_blocks,
-                                            num_kv_heads, kvh, qk_scale, lane);
+    bad = mfma_segment_rows<E, KV, D, NT, false>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, 0,
+                                                  last_pos / BS + 1, (first_pos + 1) / BS, row_last, L - 1,
+                                                  num_blocks, num_kv_heads, kvh, qk_scale, lane);
   }
   // rows r = 4*(l/16) + i of the accumulator: token tok0 + r/G, head r%G
   const float l_row = rows_sum(st.l_part);
@@ -681,17 +777,8 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   const int my_tok = tok0 + c / G;
   const bool row_live = my_tok < n;
   MfmaState<D> st;
-  {
-    const char* qrow = static_cast<const char*>(query) +
-                       ((int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G) * SH::kRow;
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-      st.qb[k] = row_live ? *reinterpret_cast<const u32x4*>(qrow + 2 * IO::q_elem(g, k)) : u32x4{0u, 0u, 0u, 0u};
-    st.m_ref = -INFINITY;
-    st.l_part = 0.f;
-#pragma unroll
-    for (int T = 0; T < VE; ++T) st.acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  mfma_begin_row<Kv16, D>(st, query, (int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G, row_live,
+                          g);
   const int my_first = L - n + tok0, my_last = L - n + min(tok0 + TPT, n) - 1;
   const int my_b_end = active ? my_last / BS + 1 : 0;
   const int my_mask_from = (my_first + 1) / BS;

@@ -146,6 +146,12 @@ size_t balanced_workspace_bytes(int num_seqs, int num_heads, int head_size) {
   return balanced_seq_bytes(num_seqs) + (size_t)kSkWorkgroups * num_heads * 2 * (head_size + kRecHead) * sizeof(float);
 }
 
+// Balanced split of multi-token queries: 16 record rows per wave instead of G.
+size_t balanced_mq_workspace_bytes(int num_seqs, int num_kv_heads, int head_size) {
+  return balanced_seq_bytes(num_seqs) +
+         (size_t)kSkWorkgroups * num_kv_heads * 2 * 16 * (head_size + kRecHead) * sizeof(float);
+}
+
 // Largest divisor of num_kv_heads that is at most 8: kv heads per workgroup.
 int heads_per_workgroup(int num_kv_heads) {
   for (int d = 8; d > 1; --d)
@@ -366,11 +372,44 @@ int prefill_group(int group, void* out, const void* query, const void* kc, const
   }
 }
 
+template <class E, class KV, int D, int G>
+int launch_mq_split(void* out, const void* query, const void* kc, const void* vc, const int32_t* bt,
+                    const int32_t* sl, const int32_t* qs, int num_seqs, int num_heads, int num_kv_heads,
+                    int max_blocks, int num_blocks, int max_q, float qk_scale, float v_scale, bool nt, void* ws,
+                    hipStream_t st) {
+  const int hpw = heads_per_workgroup(num_kv_heads);
+  const int groups = num_kv_heads / hpw;
+  const int nwg = kSkWorkgroups / groups > 0 ? kSkWorkgroups / groups : 1;
+  int4* ws_seq = static_cast<int4*>(ws);
+  float* ws_rec = reinterpret_cast<float*>(static_cast<char*>(ws) + balanced_seq_bytes(num_seqs));
+  const size_t lds = (size_t)2 * (num_seqs + 1) * sizeof(int);
+  auto k = nt ? pa_decode_sk_kernel<E, KV, D, G, true, true> : pa_decode_sk_kernel<E, KV, D, G, false, true>;
+  hipLaunchKernelGGL(k, dim3((unsigned)(groups * nwg)), dim3(64 * hpw), lds, st, out, query,
+                     static_cast<const char*>(kc), static_cast<const char*>(vc), bt, sl, num_seqs, num_heads,
+                     num_kv_heads, max_blocks, num_blocks, qk_scale, v_scale, hpw, nwg, ws_seq, ws_rec, qs);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  const long long grid = (long long)num_seqs * max_q * num_heads;
+  hipLaunchKernelGGL((pa_sk_merge_mq_kernel<E, D, G>), dim3((unsigned)grid), dim3(64), 0, st, out, ws_seq, ws_rec,
+                     qs, num_heads, hpw, nwg, max_q);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// Which path a multi-token call takes, and the workspace it needs.
+bool prefill_uses_split(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
+  return max_q * (num_heads / num_kv_heads) <= 16 && num_seqs <= kSkMaxSeqs;
+}
+
+size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_q) {
+  return prefill_uses_split(num_seqs, num_heads, num_kv_heads, max_q)
+             ? balanced_mq_workspace_bytes(num_seqs, num_kv_heads, head_size) : 0;
+}
+
 int prefill_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
                  const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start, int num_seqs,
                  int num_query_tokens, int num_heads, int num_kv_heads, int head_size, int block_size,
                  int max_blocks_per_seq, int num_blocks, int max_query_len, float scale, int dtype, unsigned flags,
-                 void* stream, bool fp8_kv, float k_scale, float v_scale) {
+                 void* workspace, size_t workspace_bytes, void* stream, bool fp8_kv, float k_scale,
+                 float v_scale) {
   if (num_seqs < 0 || num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
       block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0 || max_query_len < 0)
     return PA_ERR_INVALID_ARG;
@@ -393,6 +432,22 @@ int prefill_impl(void* out, const void* query, const void* k_cache, const void* 
   const float qks = (float)((double)scale * (double)k_scale * 1.4426950408889634);
   const bool nt = (flags & PA_FLAG_SHARED_BLOCKS) == 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (prefill_uses_split(num_seqs, num_heads, num_kv_heads, mq)) {
+    const size_t need = balanced_mq_workspace_bytes(num_seqs, num_kv_heads, head_size);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PA_ERR_WORKSPACE;
+#define PA_MQ(E, KV, D, G) launch_mq_split<E, KV, D, G>(out, query, k_cache, v_cache, block_tables, seq_lens, \
+    query_start, num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_blocks, mq, qks, v_scale, nt, workspace, st)
+#define PA_MQ_G(E, KV, D) (group == 1 ? PA_MQ(E, KV, D, 1) : group == 2 ? PA_MQ(E, KV, D, 2) : \
+                           group == 4 ? PA_MQ(E, KV, D, 4) : PA_MQ(E, KV, D, 8))
+    if (dtype == PA_F16) {
+      if (fp8_kv) return head_size == 64 ? PA_MQ_G(ElemF16, KvFp8, 64) : PA_MQ_G(ElemF16, KvFp8, 128);
+      return head_size == 64 ? PA_MQ_G(ElemF16, Kv16, 64) : PA_MQ_G(ElemF16, Kv16, 128);
+    }
+    if (fp8_kv) return head_size == 64 ? PA_MQ_G(ElemBF16, KvFp8, 64) : PA_MQ_G(ElemBF16, KvFp8, 128);
+    return head_size == 64 ? PA_MQ_G(ElemBF16, Kv16, 64) : PA_MQ_G(ElemBF16, Kv16, 128);
+#undef PA_MQ_G
+#undef PA_MQ
+  }
 #define PA_PREFILL(E, KV, D) prefill_group<E, KV, D>(group, out, query, k_cache, v_cache, block_tables, seq_lens, \
     query_start, num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_blocks, mq, qks, v_scale, nt, st)
   if (dtype == PA_F16) {
@@ -517,15 +572,26 @@ extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+extern "C" size_t pa_prefill_workspace_size(int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
+                                            int head_size, int max_query_len) {
+  if (num_seqs <= 0 || num_query_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      max_query_len < 0 || num_heads % num_kv_heads != 0)
+    return 0;
+  const int mq = max_query_len > 0 ? max_query_len : num_query_tokens;
+  return pa::prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_size, mq);
+}
+
 extern "C" int paged_attention_prefill(void* out, const void* query, const void* k_cache, const void* v_cache,
                                        const int32_t* block_tables, const int32_t* seq_lens,
                                        const int32_t* query_start, int num_seqs, int num_query_tokens,
                                        int num_heads, int num_kv_heads, int head_size, int block_size,
                                        int max_blocks_per_seq, int num_blocks, int max_query_len, float scale,
-                                       int dtype, unsigned flags, void* stream) {
+                                       int dtype, unsigned flags, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
   return pa::prefill_impl(out, query, k_cache, v_cache, block_tables, seq_lens, query_start, num_seqs,
                           num_query_tokens, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
-                          num_blocks, max_query_len, scale, dtype, flags, stream, false, 1.0f, 1.0f);
+                          num_blocks, max_query_len, scale, dtype, flags, workspace, workspace_bytes, stream, false,
+                          1.0f, 1.0f);
 }
 
 extern "C" int paged_attention_prefill_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -533,9 +599,11 @@ extern "C" int paged_attention_prefill_fp8(void* out, const void* query, const v
                                            const int32_t* query_start, int num_seqs, int num_query_tokens,
                                            int num_heads, int num_kv_heads, int head_size, int block_size,
                                            int max_blocks_per_seq, int num_blocks, int max_query_len, float scale,
-                                           float k_scale, float v_scale, int dtype, unsigned flags, void* stream) {
+                                           float k_scale, float v_scale, int dtype, unsigned flags,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
   if (!pa::positive_finite(k_scale) || !pa::positive_finite(v_scale)) return PA_ERR_INVALID_ARG;
   return pa::prefill_impl(out, query, k_cache, v_cache, block_tables, seq_lens, query_start, num_seqs,
                           num_query_tokens, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
-                          num_blocks, max_query_len, scale, dtype, flags, stream, true, k_scale, v_scale);
+                          num_blocks, max_query_len, scale, dtype, flags, workspace, workspace_bytes, stream, true,
+                          k_scale, v_scale);
 }

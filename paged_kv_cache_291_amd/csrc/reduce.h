@@ -149,4 +149,37 @@ pa_sk_merge_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, cons
   write_row<E, D>(out, sh, res);
 }
 
+// Balanced split with several query tokens per sequence (rows = (token,
+// head) pairs, 16 record rows per wave): one wave per (sequence, token slot
+// i < max_q, query head); slots past the sequence's query rows and sequences
+// written whole by the decode kernel return at once.
+template <class E, int D, int G>
+__global__ void __launch_bounds__(64)
+pa_sk_merge_mq_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, const float* __restrict__ ws_rec,
+                      const int* __restrict__ query_start, int num_heads, int hpw, int nwg, int max_q) {
+  constexpr int REC = rec_floats<D>();
+  constexpr int PER = D / 64;
+  const int64_t id = blockIdx.x;
+  const int h = (int)(id % num_heads);
+  const int64_t t = id / num_heads;
+  const int i = (int)(t % max_q), s = (int)(t / max_q);
+  const int a = query_start[s], nq = query_start[s + 1] - a;
+  if (i >= nq) return;
+  const int4 e = ws_seq[s];
+  if (e.x < 0) return;
+  const int w1 = e.x, c0 = e.y, c1 = e.z, U = e.w;
+  const int n = sk_owner(c1 - 1, U, nwg) - w1 + 1;
+  const int kvh = h / G, r = i * G + h % G;
+  const int hg = kvh / hpw, wv = kvh - hg * hpw;
+  const int first_slot = sk_range_begin(w1, U, nwg) < c0 ? 1 : 0;
+  auto rec_of = [&](int j) {
+    const int w = w1 + j, slot = j == 0 ? first_slot : 0;
+    return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * 16 + r) * REC;
+  };
+  float res[PER];
+  lse_merge<D>(rec_of, [&](int j) { return sk_range_begin(w1 + j, U, nwg) != sk_range_begin(w1 + j + 1, U, nwg); },
+               n, res);
+  write_row<E, D>(out, (int64_t)(a + i) * num_heads + h, res);
+}
+
 }  // namespace pa

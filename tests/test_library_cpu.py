@@ -63,6 +63,7 @@ def _decode(lib, **kw):
 
 
 FAKE = 0x1000  # a non-null, aligned address that is never dereferenced on the host
+FAKE_WS = 0x10000  # same, 256-byte aligned
 
 
 def test_decode_host_errors():
@@ -129,14 +130,20 @@ def test_fp8_host_errors():
 
 def test_prefill_host_errors():
     lib = P.load_library()
-    f = lambda dtype=2, S=4, T=8, D=128, BS=16, Hq=8, Hkv=2, mq=0, qs=FAKE, ptr=FAKE: lib.paged_attention_prefill(
-        ptr, FAKE, FAKE, FAKE, FAKE, FAKE, qs, S, T, Hq, Hkv, D, BS, 8, 64, mq, 0.1, dtype, 0, None)
+    f = lambda dtype=2, S=4, T=8, D=128, BS=16, Hq=8, Hkv=2, mq=0, qs=FAKE, ptr=FAKE, ws=FAKE_WS, wsb=1 << 30: \
+        lib.paged_attention_prefill(ptr, FAKE, FAKE, FAKE, FAKE, FAKE, qs, S, T, Hq, Hkv, D, BS, 8, 64, mq, 0.1, dtype,
+                                    0, ws, wsb, None)
     assert f(S=0) == 0 and f(T=0) == 0                            # nothing to do
     assert f(dtype=0) == -2 and f(dtype=3) == -1                  # fp32 not built; fp8 is not a query type
     assert f(qs=None) == -1 and f(ptr=None) == -1 and f(mq=-1) == -1
     assert f(D=96) == -2 and f(BS=32) == -2 and f(Hq=12, Hkv=8) == -1
+    assert f(mq=4, ws=None) == -3 and f(mq=4, wsb=16) == -3      # 4 tokens x 4 heads: split path needs a workspace
     assert lib.paged_attention_prefill_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, 2, 128, 16, 8, 64, 0,
-                                           0.1, 0.0, 1.0, 2, 0, None) == -1   # scale must be positive
+                                           0.1, 0.0, 1.0, 2, 0, None, 0, None) == -1   # scale must be positive
+    # workspace: split path iff max_query_len * group <= 16
+    assert P.pa_prefill_workspace_size(256, 1024, 32, 8, 128, 4) == 4096 + 256 * 8 * 2 * 16 * 132 * 4
+    assert P.pa_prefill_workspace_size(8, 4096, 32, 8, 128, 512) == 0
+    assert P.pa_prefill_workspace_size(3, 6, 8, 8, 64, 0) == 256 + 256 * 8 * 2 * 16 * 68 * 4   # 0: T = 6 rows
 
 
 def test_python_binding_refuses_host_tensors():

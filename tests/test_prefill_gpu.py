@@ -128,3 +128,49 @@ def test_few_query_rows_per_sequence(dtype, D, Hq, Hkv, fp8):
     print(f"verify-shaped {dtype} D={D} {Hq}/{Hkv} fp8={fp8}: max-abs {diff.max():.3e}", flush=True)
     assert np.isfinite(g).all()
     assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
+
+
+def test_verify_8b_batch_full_size():
+    """Speculative verification on the 8B-shaped batch (4 query rows per
+    sequence): the balanced split with causal rows, sampled rows against
+    decode over the sequence cut after each row's position."""
+    wl = W.make_config(3, 0, poison=True)
+    S = wl.num_seqs
+    nq = np.full(S, 4, np.int32)
+    starts = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = W.random_rows(3, 900, (int(starts[-1]), wl.num_heads, wl.head_size), "bf16")
+    g = _gpu(wl, starts, q, max_q=4)
+    assert np.isfinite(g).all()
+    kc, vc, qr = W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache), W.raw_numpy(q)
+    worst = 0.0
+    for s in sample_seqs_idx(wl, 10):
+        for i in range(4):
+            row = starts[s] + i
+            cut = np.array([wl.seq_lens[s] - 4 + i + 1], np.int32)
+            want = oracle.paged_decode_ref(qr[row:row + 1], kc, vc, wl.block_tables[s:s + 1], cut, wl.scale, "bf16")
+            d = np.abs(g[row] - want[0])
+            worst = max(worst, float(d.max()))
+            assert np.all(d <= TOL["bf16"] + HALF_ULP["bf16"] * np.abs(want[0])), (s, i)
+    print(f"verify 8B batch: max-abs {worst:.3e} on sampled rows", flush=True)
+
+
+def sample_seqs_idx(wl, n):
+    from helpers import sample_seqs
+    return sample_seqs(wl, n)
+
+
+def test_split_path_contract_violations():
+    lens, nq = [40, 20, 30, 50, 16], [3, 4, 2, 4, 1]
+    wl, starts, q = _case(73, 8, 2, 64, "bf16", lens, nq)
+    bt, sl = wl.block_tables.copy(), wl.seq_lens.copy()
+    sl[1] = 3                                             # fewer tokens than query rows
+    sl[2] = bt.shape[1] * 16 + 1                          # past the table row
+    bt[3, 1] = wl.num_blocks                              # id outside the pool
+    g = _gpu(wl, starts, q, bt=bt, sl=sl, max_q=4)        # 4 rows x 4 heads: the split path
+    for s in (1, 2, 3):
+        assert np.isnan(g[starts[s]:starts[s + 1]]).all(), s
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                   wl.block_tables, wl.seq_lens, starts, wl.scale, "bf16", seqs=[0, 4])
+    for s in (0, 4):
+        r = slice(starts[s], starts[s + 1])
+        assert np.max(np.abs(g[r] - ref[r])) <= TOL["bf16"] + HALF_ULP["bf16"] * np.max(np.abs(ref[r]))
