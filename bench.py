@@ -322,7 +322,8 @@ def bench_prefill(args):
         "config": {"workload": desc, "query_tokens": T, "kv_bytes": kv, "flops": flops},
         "roofline": ({"bound": "hbm", "achieved": round(kv / launch / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(kv / launch / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                      "kernel": "pa_prefill_kernel", "bytes_per_launch": kv}
+                      "kernel": "pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel",
+                      "bytes_per_launch": kv}
                      if args.prefill_case == "verify" else
                      {"bound": "mfma", "achieved": round(flops / launch / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(flops / launch / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
