@@ -13,12 +13,14 @@
  * A block holds the K/V of 16 tokens (aiflowlearn.net vLLM course page,
  * section on cutting the KV cache into pages).
  *
- * Conventions for every entry point:
+ * Conventions for the device entry points (the host block manager pa_bm_*
+ * at the end has its own):
  *  - All data pointers are DEVICE pointers owned by the caller; the library
  *    never allocates or frees, keeps no global state, and is re-entrant.
  *  - Tensors are dense and row-major in the shapes given; q, caches and
- *    outputs share one element type (enum pa_dtype).  Data pointers must be
- *    16-byte aligned.
+ *    outputs share one element type (enum pa_dtype) except where an entry
+ *    point says otherwise (fp8 pools).  Data pointers must be 16-byte
+ *    aligned.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
  *    enqueue work on it; there is no host synchronisation.
  *  - Errors that the host can see (null pointer, unsupported size or type,

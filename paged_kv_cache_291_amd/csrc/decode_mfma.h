@@ -1,4 +1,5 @@
-// Paged decode on the matrix cores (16-bit KV: bf16, fp16).
+// Paged attention on the matrix cores: bf16/fp16 queries over 16-bit or fp8
+// (e4m3) K/V pools.
 //
 // One wave works on one (sequence, kv head) at a time; per 16-token block:
 //   QK:  S^T[t][h] = sum_d K[t][d] Q[h][d]: 16x16x32 MFMAs over head_size,
@@ -17,15 +18,21 @@
 //        more than 2^8; until then probabilities are taken against the stale
 //        reference, which is the same sum re-associated.
 //
-// Two launch shapes share this core:
-//  * pa_decode_mfma_kernel: one wave per (sequence, kv head, partition) -
-//    the split-context path with a fixed partition size.
+// The K/V format only changes the loader (KvIo: where each lane's bytes are
+// and how they become MFMA operands).  Launch shapes sharing this core:
 //  * pa_decode_sk_kernel: balanced split.  The (sequence, block) pairs of the
 //    whole batch are laid end to end and cut into equal ranges, one per
 //    workgroup; a workgroup has one wave per kv head of a head group, so a
-//    block's heads (one contiguous stretch of the pool) are read together.
-//    A sequence that crosses a range boundary leaves partial records that a
-//    merge kernel combines.
+//    block's heads (one contiguous stretch of the pool) are read together,
+//    with the waves kept in step.  A sequence that crosses a range boundary
+//    leaves partial records that a merge kernel combines.  With MQ the 16
+//    rows are (token, head) pairs of several query tokens (speculative
+//    verification), masked causally on the final blocks.
+//  * pa_decode_mfma_kernel: one workgroup per (sequence, partition, head
+//    group) - the split-context path with a fixed partition size.
+//  * pa_prefill_kernel / pa_prefill_lds_kernel: multi-token queries, one
+//    wave per 16-row tile; the LDS variant shares each K/V block among 8
+//    tiles.
 #pragma once
 
 #include "common.h"
