@@ -194,3 +194,25 @@ def test_workspace_reuse_and_empty_batches():
     g = _decode_with(wbad, ws)
     assert np.isnan(g[2]).all()
     assert (np.delete(g, 2, axis=0) == 0).all()
+
+
+def test_largest_batch_balanced_split():
+    """16383 sequences, the most the balanced split takes (its prefix sums
+    fill 64 KiB of LDS; the multi-token variant stages twice that): decode and
+    one-row multi-token calls against the oracle on sampled sequences."""
+    S = 16383
+    lens = (np.arange(S) % 5).astype(np.int32) + 1
+    wl = W.make_random(9, S, 8, 2, 64, "bf16", lens)
+    d = to_device(wl)
+    out = torch.empty_like(d["q"])
+    P.paged_attention_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale, max_seq_len=wl.max_seq_len)
+    out2 = torch.empty_like(d["q"])
+    P.paged_attention_prefill(out2, d["q"], d["kc"], d["vc"], d["bt"], d["sl"],
+                              torch.arange(0, S + 1, dtype=torch.int32, device="cuda"), wl.scale, max_query_len=1)
+    torch.cuda.synchronize()
+    seqs = [0, 1, 7, 4097, 8000, S - 2, S - 1]
+    ref = oracle_decode(wl, seqs=seqs)
+    for o in (out, out2):
+        g = o.cpu().double().numpy()[seqs]
+        assert np.all(np.abs(g - ref) <= TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref))
+    assert torch.isfinite(out.float()).all() and torch.isfinite(out2.float()).all()
