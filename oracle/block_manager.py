@@ -22,9 +22,9 @@ Sources (pages on the subject, cited by title and section):
 
 Readings where the pages are silent (each is listed in the design notes):
 
-* the free pool is a stack: the block freed last is handed out first (the
-  figure's "freed blocks go straight to a new request"); a new pool hands out
-  block 0 first, then 1, 2, ...;
+* the free pool is a stack: the block freed last is handed out first (in the
+  figure, blocks a finished request frees are handed straight to the next
+  one); a new pool hands out block 0 first, then 1, 2, ...;
 * a sequence's blocks are released in table order (logical block 0 first), so
   its last block is on top of the pool afterwards;
 * token t of a sequence goes to slot ``table[t // block_size] * block_size +
