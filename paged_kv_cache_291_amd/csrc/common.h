@@ -296,6 +296,28 @@ __device__ inline float rows_max(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// max(a, b) for values that are never NaN (scores, -inf for masked keys) in
+// one instruction: the median of (a, b, +inf).  Written with fmaxf, every
+// input that the compiler cannot prove canonical (matrix-core results, lane
+// swaps) is first quieted by an extra instruction.  The +inf is hidden from
+// the compiler (an SGPR it cannot see through), which would otherwise turn the
+// median back into fmaxf.
+__device__ inline float opaque_inf() {
+  float v = INFINITY;
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+__device__ inline float max_nonan(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
+
+// rows_max for values that are never NaN.
+__device__ inline float rows_max_nonan(float v, float inf) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max_nonan(__uint_as_float(a[0]), __uint_as_float(a[1]), inf);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_nonan(__uint_as_float(b[0]), __uint_as_float(b[1]), inf);
+}
+
 __device__ inline float rows_sum(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -314,6 +336,7 @@ struct Mfma;
 
 template <>
 struct Mfma<ElemBF16> {
+  static constexpr uint32_t kOnes = 0x3F803F80u;   // two 1.0 elements
   __device__ static f32x4 qk(const u32x4& a, const u32x4& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
@@ -324,6 +347,7 @@ struct Mfma<ElemBF16> {
 
 template <>
 struct Mfma<ElemF16> {
+  static constexpr uint32_t kOnes = 0x3C003C00u;
   __device__ static f32x4 qk(const u32x4& a, const u32x4& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }

@@ -731,26 +731,40 @@ pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const 
 
 // ---- multi-token queries, K/V shared through LDS
 
-// Blocks per LDS stage and the padded row pitch (bytes) of a 16-bit K/V row
-// in LDS: 16 extra bytes shift consecutive rows by four banks, so the 16
-// lanes reading one MFMA operand (16 rows, same column) hit different banks.
+// LDS stage of kPfStageBlocks blocks (16-bit elements whatever the pool type):
+//  * K rows of each block at a padded pitch: 16 extra bytes shift consecutive
+//    rows by four banks, so the 16 lanes reading one MFMA operand (16 rows,
+//    same column) hit different banks;
+//  * V of each pair of blocks (2p, 2p+1) laid out as the PV step reads it:
+//    per key quad q (keys 4q..4q+3 of both blocks), one 16-byte entry per
+//    head dimension d holding V[4q..4q+3][d] of block 2p then of block 2p+1,
+//    entries ordered (d % VE, d / VE) so that the 16 lanes of one PV operand
+//    read 256 consecutive bytes.
 constexpr int kPfStageBlocks = 4;
 template <int D> constexpr int pf_row_pitch() { return D * 2 + 16; }
-template <int D> constexpr int pf_stage_bytes() { return kPfStageBlocks * 2 * kBlockSize * pf_row_pitch<D>(); }
+template <int D> constexpr int pf_k_bytes() { return kPfStageBlocks * kBlockSize * pf_row_pitch<D>(); }
+template <int D> constexpr int pf_v_quad_bytes() { return D * 16; }
+template <int D> constexpr int pf_v_pair_bytes() { return 4 * pf_v_quad_bytes<D>(); }
+template <int D> constexpr int pf_stage_bytes() { return pf_k_bytes<D>() + kPfStageBlocks / 2 * pf_v_pair_bytes<D>(); }
 
 // Grid: one workgroup of 8 waves per (sequence, kv head, 8 consecutive query
 // tiles); wave w owns tile 8*grp + w (16 (token, head) rows as in
 // pa_prefill_kernel).  The workgroup streams the sequence's blocks in stages
-// of kPfStageBlocks: all 512 threads copy a stage's K and V rows of this kv
-// head into LDS (double-buffered, one barrier per stage; fp8 codes are
-// widened to the query type on the way; rows past the sequence end are
-// zero), then every wave consumes the stage's blocks it can see.  Each K/V
-// byte is read from memory once per 8 tiles instead of once per tile.
-// The linear workgroup id is split so that all workgroups of one (sequence,
-// kv head) land on the same XCD (workgroups are dealt to the 8 XCDs round
-// robin), where its K/V stay in that XCD's L2.
+// of kPfStageBlocks, double-buffered in LDS with one barrier per stage: wave
+// w copies block w%4 of the next stage, K (w < 4) or V (w >= 4), while every
+// wave consumes the current stage's blocks it can see, two blocks per step:
+//   QK: two 16-key score tiles (16x16x32 MFMAs over head_size);
+//   PV: one 16x16x32 MFMA per 16 output columns over the pair's 32 keys, and
+//       one more against a column of ones, which sums each row's weights as
+//       rounded for the PV step (the softmax denominator).
+// Each K/V byte is read from memory once per 8 tiles instead of once per
+// tile.  Rows past the sequence end, blocks past the workgroup's last block
+// and out-of-pool block ids load as zeros (the buffer range of the block is
+// cut to its valid rows).  The linear workgroup id is split so that all
+// workgroups of one (sequence, kv head) land on the same XCD (workgroups are
+// dealt to the 8 XCDs round robin), where its K/V stay in that XCD's L2.
 template <class E, class KV, int D, int G, bool NT>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8)))
 pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, const char* __restrict__ k_cache,
                       const char* __restrict__ v_cache, const int* __restrict__ block_tables,
                       const int* __restrict__ seq_lens, const int* __restrict__ query_start, int num_seqs,
@@ -758,17 +772,19 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
                       float qk_scale, float v_scale) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
-  using IO = KvIo<Kv16, ElemBF16, D>;                 // the query map of 16-bit K rows (LDS holds 16-bit rows)
-  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe, VW = SH::kVw;
-  constexpr int RP = pf_row_pitch<D>();
+  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe;
+  constexpr int RP = pf_row_pitch<D>(), KB = pf_k_bytes<D>(), QB = pf_v_quad_bytes<D>(), PB = pf_v_pair_bytes<D>();
+  constexpr int SB = pf_stage_bytes<D>();
   constexpr int KVB = KV::kBytes;                     // bytes per element in the pools
   constexpr int CPR = D * KVB / 16;                   // 16-byte chunks per pool row
-  constexpr int CHUNKS = kPfStageBlocks * 2 * BS * CPR;
-  constexpr int PER_T = CHUNKS / 512;                 // chunks per thread and stage
-  static_assert(CHUNKS % 512 == 0, "stage must split evenly over the workgroup");
-  __shared__ __align__(16) char smem[2 * pf_stage_bytes<D>()];
+  constexpr int DPC = 16 / KVB;                       // elements per chunk
+  constexpr int KC = CPR / 4;                         // K chunks per lane: a wave copies a block's 16 rows
+  constexpr int VL = 4 * CPR;                         // lanes copying V: one (key quad, chunk column) each
+  static_assert(kPfStageBlocks == 4 && KC >= 1 && VL <= 64 && DPC % VE == 0, "stage layout");
+  __shared__ __align__(16) char smem[2 * SB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets block loads use SGPR descriptors
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int pair = (slot / groups_per_pair) * 8 + xcd, grp = slot % groups_per_pair;
   if (pair >= num_seqs * num_kv_heads) return;
@@ -786,74 +802,124 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   MfmaState<D> st;
   mfma_begin_row<Kv16, D>(st, query, (int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G, row_live,
                           g);
+  // scores are scaled after the max (one multiply per row instead of one per
+  // score), which needs a non-negative scale: a negative one moves its sign
+  // into the query (exact)
+  if (qk_scale < 0.f) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) st.qb[k] ^= 0x80008000u;
+    qk_scale = -qk_scale;
+  }
+  f32x4 acc_l = {0.f, 0.f, 0.f, 0.f};                // row sums of the rounded weights, rows as acc
+  const u32x4 ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
+  const float inf = opaque_inf();
   const int my_first = L - n + tok0, my_last = L - n + min(tok0 + TPT, n) - 1;
   const int my_b_end = active ? my_last / BS + 1 : 0;
-  const int my_mask_from = (my_first + 1) / BS;
+  const int my_p_end = (my_b_end + 1) / 2;            // block pairs this wave consumes
+  const int my_p_open = ((my_first + 1) / BS) / 2;    // pairs before this one are visible to every row
   const int row_last = L - n + min(my_tok, n - 1);
   const int wg_last = L - n + min(wg_tok0 + 8 * TPT, n) - 1;
   const int wg_b_end = bad_len ? 0 : wg_last / BS + 1;
   const int* bt_row = block_tables + (int64_t)s * max_blocks;
-  const int blk_bytes = BS * num_kv_heads * D * KVB;
 
-  // one stage: PER_T chunks per thread, chunk q -> (block, K|V, row, column)
-  u32x4 regs[PER_T];
+  // staging role of this wave: block `sblk` of every stage, K or V
+  const bool v_role = wave >= 4;
+  const int sblk = wave & 3;
+  const int row_stride = num_kv_heads * D * KVB;
+  const int blk_bytes = BS * row_stride;
+  const int head_off = kvh * D * KVB;
+  const char* pool = v_role ? v_cache : k_cache;
+  const bool v_lane = lane < VL;
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!v_role) {
+      const int q = lane + 64 * (i % KC);             // K chunk: row q / CPR, column q % CPR
+      voff[i] = (q / CPR) * row_stride + head_off + (q % CPR) * 16;
+    } else {                                          // V: key 4*quad + i, column lane % CPR
+      voff[i] = (4 * (lane / CPR) + i) * row_stride + head_off + (lane % CPR) * 16;
+    }
+  }
+
+  u32x4 regs[4];
+  int ids = 0;                                        // block ids of the current window of 64 blocks
   bool bad_id = false;
   auto issue = [&](int stage) {
+    const int bi = stage * kPfStageBlocks + sblk;
+    if ((stage & 15) == 0) {                          // stage * 4 is a multiple of 64: a new window
+      const int idx = stage * kPfStageBlocks + lane;
+      ids = idx < wg_b_end ? bt_row[idx] : 0;
+      bad_id |= __ballot(idx < wg_b_end && (unsigned)ids >= (unsigned)num_blocks) != 0;
+    }
+    const int id = __builtin_amdgcn_readlane(ids, bi & 63);
+    const bool ok = bi < wg_b_end && (unsigned)id < (unsigned)num_blocks;
+    const int rows = ok ? min(BS, L - bi * BS) : 0;
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(pool + (int64_t)(ok ? id : 0) * blk_bytes, rows * row_stride);
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int q = tid + 512 * i;
-      const int col = q % CPR, row = (q / CPR) % BS, kv = (q / (CPR * BS)) & 1, blk = q / (CPR * BS * 2);
-      const int bi = stage * kPfStageBlocks + blk;
-      const int tok = bi * BS + row;
-      regs[i] = u32x4{0u, 0u, 0u, 0u};
-      if (bi < wg_b_end && tok < L) {
-        const int id = bt_row[bi];
-        if ((unsigned)id < (unsigned)num_blocks) {
-          const char* base = (kv ? v_cache : k_cache) + (int64_t)id * blk_bytes + (row * num_kv_heads + kvh) * D * KVB;
-          regs[i] = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + col)
-                       : reinterpret_cast<const u32x4*>(base)[col];
-        } else {
-          bad_id = true;
+    for (int i = 0; i < 4; ++i)
+      if (v_role ? v_lane : i < KC) regs[i] = load16<NT>(r, voff[i], 0);
+  };
+  // word w (elements 2w, 2w+1) of a staged chunk as 16-bit elements
+  auto word = [&](const u32x4& x, int w) -> uint32_t {
+    if constexpr (KVB == 2) return x[w];
+    else return (w & 1) ? fp8x2_to<E, true>(x[w >> 1]) : fp8x2_to<E, false>(x[w >> 1]);
+  };
+  auto commit = [&](int buf) {
+    char* sb = smem + buf * SB;
+    if (!v_role) {
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        const int q = lane + 64 * i;
+        char* dst = sb + (sblk * BS + q / CPR) * RP + (q % CPR) * DPC * 2;
+#pragma unroll
+        for (int h = 0; h < DPC / 8; ++h)
+          *reinterpret_cast<u32x4*>(dst + 16 * h) =
+              u32x4{word(regs[i], 4 * h), word(regs[i], 4 * h + 1), word(regs[i], 4 * h + 2), word(regs[i], 4 * h + 3)};
+      }
+    } else if (v_lane) {
+      const int col = lane % CPR;
+      char* dst = sb + KB + (sblk >> 1) * PB + (lane / CPR) * QB + (sblk & 1) * 8 + col * (DPC / VE) * 16;
+#pragma unroll
+      for (int w = 0; w < DPC / 2; ++w) {
+        const uint32_t k0 = word(regs[0], w), k1 = word(regs[1], w), k2 = word(regs[2], w), k3 = word(regs[3], w);
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const int e = 2 * w + hi;                   // element of the chunk: d = col * DPC + e
+          const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+          *reinterpret_cast<u32x2*>(dst + ((e % VE) * 16 + e / VE) * 16) =
+              u32x2{__builtin_amdgcn_perm(k1, k0, sel), __builtin_amdgcn_perm(k3, k2, sel)};
         }
       }
     }
   };
-  auto commit = [&](int buf) {
-    char* sb = smem + buf * pf_stage_bytes<D>();
+
+  // Blocks 2p, 2p+1 of a stage; key0: position of block 2p's first key.
+  // Every row sees key 0, and the first pair is consumed before any other,
+  // so m_ref is finite whenever weights are taken.
+  auto consume = [&](auto masked_tag, const char* sb, int p, int key0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* ka = sb + 2 * p * BS * RP + c * RP + 16 * g;
+    const char* kb = ka + BS * RP;
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sbk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int q = tid + 512 * i;
-      const int col = q % CPR, row = (q / CPR) % BS, kv = (q / (CPR * BS)) & 1, blk = q / (CPR * BS * 2);
-      char* dst = sb + ((blk * 2 + kv) * BS + row) * RP;
-      if constexpr (KVB == 2) {
-        *reinterpret_cast<u32x4*>(dst + col * 16) = regs[i];
-      } else {                                        // 16 codes -> 16 elements of E
-        const u32x4 w = regs[i];
-        const u32x4 lo = {fp8x2_to<E, false>(w[0]), fp8x2_to<E, true>(w[0]), fp8x2_to<E, false>(w[1]),
-                          fp8x2_to<E, true>(w[1])};
-        const u32x4 hi = {fp8x2_to<E, false>(w[2]), fp8x2_to<E, true>(w[2]), fp8x2_to<E, false>(w[3]),
-                          fp8x2_to<E, true>(w[3])};
-        *reinterpret_cast<u32x4*>(dst + col * 32) = lo;
-        *reinterpret_cast<u32x4*>(dst + col * 32 + 16) = hi;
-      }
+    for (int k = 0; k < KS; ++k) {
+      sa = M::qk(*reinterpret_cast<const u32x4*>(ka + 64 * k), st.qb[k], sa);
+      sbk = M::qk(*reinterpret_cast<const u32x4*>(kb + 64 * k), st.qb[k], sbk);
     }
-  };
-  auto consume = [&](const char* kb, const char* vb, int key0, bool masked) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    // lane l holds raw scores of row l%16, keys key0 + 16*(i/4) + 4*(l/16) + i%4
+    float z[8] = {sa[0], sa[1], sa[2], sa[3], sbk[0], sbk[1], sbk[2], sbk[3]};
+    bool vis[8];
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
-      sc = M::qk(*reinterpret_cast<const u32x4*>(kb + c * RP + 64 * k + 16 * g), st.qb[k], sc);
-    float z[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = sc[i] * qk_scale;
-      if (masked && key0 + 4 * g + i > row_last) z[i] = -INFINITY;
+    for (int i = 0; i < 8; ++i) {
+      vis[i] = !MASKED || key0 + 16 * (i >> 2) + 4 * g + (i & 3) <= row_last;
+      if (MASKED && !vis[i]) z[i] = -INFINITY;
     }
-    const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    const float zm = max_nonan(max_nonan(max_nonan(z[0], z[1], inf), max_nonan(z[2], z[3], inf), inf),
+                               max_nonan(max_nonan(z[4], z[5], inf), max_nonan(z[6], z[7], inf), inf), inf);
+    const float bm = rows_max_nonan(zm, inf) * qk_scale;
     if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
       const float m_new = fmaxf(st.m_ref, bm);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
-      st.l_part *= alpha;
+      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);     // 0 on the first pair
       float ar[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
@@ -861,62 +927,49 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
       for (int T = 0; T < VE; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.acc[T][i] *= ar[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_l[i] *= ar[i];
       st.m_ref = m_new;
     }
-    float p[4];
+    float p8[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - st.m_ref);
-    st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    const u32x2 pa = {pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
-    uint32_t v[4][VW];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const char* vr = vb + (4 * g + j) * RP + VE * 2 * c;
-      if constexpr (VW == 4) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(vr);
-        v[j][0] = t[0]; v[j][1] = t[1]; v[j][2] = t[2]; v[j][3] = t[3];
-      } else {
-        const u32x2 t = *reinterpret_cast<const u32x2*>(vr);
-        v[j][0] = t[0]; v[j][1] = t[1];
-      }
+    for (int i = 0; i < 8; ++i) {
+      const float t = fmaf(z[i], qk_scale, -st.m_ref);
+      p8[i] = __builtin_amdgcn_exp2f(MASKED && !vis[i] ? -INFINITY : t);
     }
+    const u32x4 pa = {pack2<E>(p8[0], p8[1]), pack2<E>(p8[2], p8[3]), pack2<E>(p8[4], p8[5]), pack2<E>(p8[6], p8[7])};
+    const char* vb = sb + KB + p * PB + g * QB + c * 16;
 #pragma unroll
-    for (int T = 0; T < VE; ++T) {
-      const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;
-      const u32x2 vb2 = {__builtin_amdgcn_perm(v[1][T >> 1], v[0][T >> 1], sel),
-                         __builtin_amdgcn_perm(v[3][T >> 1], v[2][T >> 1], sel)};
-      st.acc[T] = M::pv(pa, vb2, st.acc[T]);
-    }
+    for (int T = 0; T < VE; ++T) st.acc[T] = M::qk(pa, *reinterpret_cast<const u32x4*>(vb + 256 * T), st.acc[T]);
+    acc_l = M::qk(pa, ones, acc_l);
   };
 
   const int stages = (wg_b_end + kPfStageBlocks - 1) / kPfStageBlocks;
-  if (stages > 0) {
-    issue(0);
-    commit(0);
-  }
+  issue(0);                                           // with no blocks at all it loads zeros
+  commit(0);
+  // nothing of this wave's memory reads may stay in flight into the stage
+  // loop (the query rows included): the loop's only loads are the next stage's
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int stg = 0; stg < stages; ++stg) {
     if (stg + 1 < stages) issue(stg + 1);
-    const char* sb = smem + (stg & 1) * pf_stage_bytes<D>();
+    const char* sb = smem + (stg & 1) * SB;
+    const int p_lo = 2 * stg, p_hi = min(p_lo + 2, my_p_end), p_mid = min(max(my_p_open, p_lo), p_hi);
 #pragma unroll 1
-    for (int j = 0; j < kPfStageBlocks; ++j) {
-      const int bi = stg * kPfStageBlocks + j;
-      if (bi >= my_b_end) break;
-      consume(sb + (j * 2) * BS * RP, sb + (j * 2 + 1) * BS * RP, bi * BS, bi >= my_mask_from);
-    }
+    for (int p = p_lo; p < p_mid; ++p) consume(std::false_type{}, sb, p - p_lo, p * 2 * BS);
+#pragma unroll 1
+    for (int p = p_mid; p < p_hi; ++p) consume(std::true_type{}, sb, p - p_lo, p * 2 * BS);
     if (stg + 1 < stages) commit((stg + 1) & 1);
     __syncthreads();
   }
   const bool bad = bad_len || __syncthreads_or(bad_id);
 
-  const float l_row = rows_sum(st.l_part);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;
-    const float lr = __shfl(l_row, r);
+    const int r = 4 * g + i;                          // rows r of the accumulators: token tok0 + r/G, head r%G
     const int tok = tok0 + r / G;
     if (tok >= n) continue;
-    const float inv = lr > 0.f ? v_scale / lr : 0.f;
+    const float inv = acc_l[i] > 0.f ? v_scale / acc_l[i] : 0.f;
     float o[VE];
 #pragma unroll
     for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
