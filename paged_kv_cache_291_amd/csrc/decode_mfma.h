@@ -731,40 +731,53 @@ pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const 
 
 // ---- multi-token queries, K/V shared through LDS
 
-// LDS stage of kPfStageBlocks blocks (16-bit elements whatever the pool type):
-//  * K rows of each block at a padded pitch: 16 extra bytes shift consecutive
-//    rows by four banks, so the 16 lanes reading one MFMA operand (16 rows,
-//    same column) hit different banks;
-//  * V of each pair of blocks (2p, 2p+1) laid out as the PV step reads it:
-//    per key quad q (keys 4q..4q+3 of both blocks), one 16-byte entry per
-//    head dimension d holding V[4q..4q+3][d] of block 2p then of block 2p+1,
-//    entries ordered (d % VE, d / VE) so that the 16 lanes of one PV operand
-//    read 256 consecutive bytes.
+// LDS stage of kPfStageBlocks blocks, K rows then V rows, 16-bit elements
+// whatever the pool type, each region row-major at a padded pitch:
+//  * K (pitch 2D + 16): the 16 lanes reading one QK operand (16 rows, same
+//    16 bytes) hit 16 different bank groups;
+//  * V (pitch 2D + 32): the PV operands come from transposing reads, where 8
+//    rows x 32 bytes are read together; a 32-byte shift per row keeps those
+//    in different banks.
 constexpr int kPfStageBlocks = 4;
-template <int D> constexpr int pf_row_pitch() { return D * 2 + 16; }
-template <int D> constexpr int pf_k_bytes() { return kPfStageBlocks * kBlockSize * pf_row_pitch<D>(); }
-template <int D> constexpr int pf_v_quad_bytes() { return D * 16; }
-template <int D> constexpr int pf_v_pair_bytes() { return 4 * pf_v_quad_bytes<D>(); }
-template <int D> constexpr int pf_stage_bytes() { return pf_k_bytes<D>() + kPfStageBlocks / 2 * pf_v_pair_bytes<D>(); }
+template <int D> constexpr int pf_k_pitch() { return D * 2 + 16; }
+template <int D> constexpr int pf_v_pitch() { return D * 2 + 32; }
+template <int D> constexpr int pf_k_bytes() { return kPfStageBlocks * kBlockSize * pf_k_pitch<D>(); }
+template <int D> constexpr int pf_stage_bytes() { return kPfStageBlocks * kBlockSize * (pf_k_pitch<D>() + pf_v_pitch<D>()); }
 
-// Grid: one workgroup of 8 waves per (sequence, kv head, 8 consecutive query
-// tiles); wave w owns tile 8*grp + w (16 (token, head) rows as in
-// pa_prefill_kernel).  The workgroup streams the sequence's blocks in stages
-// of kPfStageBlocks, double-buffered in LDS with one barrier per stage: wave
-// w copies block w%4 of the next stage, K (w < 4) or V (w >= 4), while every
-// wave consumes the current stage's blocks it can see, two blocks per step:
+// Transposing LDS read (gfx950): in each 16-lane group, lane 4j + q gives the
+// address of 4 consecutive 16-bit elements (row j, columns 4q..4q+3 of a
+// 4 x 16 tile); lane i gets back column i, rows 0..3.  That is the B operand
+// of a matrix-core step over 4 consecutive k from a row-major [k][n] tile.
+__device__ inline u32x2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Query tiles per wave of pa_prefill_lds_kernel (a workgroup covers 8x as many).
+constexpr int kPfTilesPerWave = 2;
+
+// Grid: one workgroup of 8 waves per (sequence, kv head, 16 consecutive query
+// tiles); wave w owns tiles 16*grp + 2w and 2w + 1 (16 (token, head) rows
+// each, as in pa_prefill_kernel).  The workgroup streams the sequence's
+// blocks in stages of kPfStageBlocks, double-buffered in LDS with one barrier
+// per stage: wave w copies blocks w%4 and w%4 + 4 of the next stage, K
+// (w < 4) or V (w >= 4), while every wave consumes the current stage's blocks
+// it can see,
+// two blocks per step, both of its tiles on each operand read from LDS:
 //   QK: two 16-key score tiles (16x16x32 MFMAs over head_size);
 //   PV: one 16x16x32 MFMA per 16 output columns over the pair's 32 keys, and
 //       one more against a column of ones, which sums each row's weights as
 //       rounded for the PV step (the softmax denominator).
-// Each K/V byte is read from memory once per 8 tiles instead of once per
+// Each K/V byte is read from memory once per 16 tiles instead of once per
 // tile.  Rows past the sequence end, blocks past the workgroup's last block
 // and out-of-pool block ids load as zeros (the buffer range of the block is
 // cut to its valid rows).  The linear workgroup id is split so that all
 // workgroups of one (sequence, kv head) land on the same XCD (workgroups are
 // dealt to the 8 XCDs round robin), where its K/V stay in that XCD's L2.
 template <class E, class KV, int D, int G, bool NT>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, const char* __restrict__ k_cache,
                       const char* __restrict__ v_cache, const int* __restrict__ block_tables,
                       const int* __restrict__ seq_lens, const int* __restrict__ query_start, int num_seqs,
@@ -772,15 +785,15 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
                       float qk_scale, float v_scale) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
-  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe;
-  constexpr int RP = pf_row_pitch<D>(), KB = pf_k_bytes<D>(), QB = pf_v_quad_bytes<D>(), PB = pf_v_pair_bytes<D>();
-  constexpr int SB = pf_stage_bytes<D>();
+  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe, TW = kPfTilesPerWave;
+  static_assert(TW == 2, "the pipelined step interleaves exactly two tiles");
+  constexpr int RP = pf_k_pitch<D>(), VP = pf_v_pitch<D>(), KB = pf_k_bytes<D>(), SB = pf_stage_bytes<D>();
   constexpr int KVB = KV::kBytes;                     // bytes per element in the pools
   constexpr int CPR = D * KVB / 16;                   // 16-byte chunks per pool row
   constexpr int DPC = 16 / KVB;                       // elements per chunk
-  constexpr int KC = CPR / 4;                         // K chunks per lane: a wave copies a block's 16 rows
-  constexpr int VL = 4 * CPR;                         // lanes copying V: one (key quad, chunk column) each
-  static_assert(kPfStageBlocks == 4 && KC >= 1 && VL <= 64 && DPC % VE == 0, "stage layout");
+  constexpr int KC = CPR / 4;                         // chunks per lane and block: 16 rows per block
+  constexpr int SBW = kPfStageBlocks / 4;             // blocks of a stage each staging wave copies
+  static_assert(kPfStageBlocks % 4 == 0 && KC >= 1, "stage layout");
   __shared__ __align__(16) char smem[2 * SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -790,74 +803,75 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   if (pair >= num_seqs * num_kv_heads) return;
   const int s = pair / num_kv_heads, kvh = pair - s * num_kv_heads;
   const int q0 = query_start[s], n = query_start[s + 1] - q0, L = seq_lens[s];
-  const int wg_tok0 = grp * 8 * TPT;
+  const int wg_tok0 = grp * 8 * TW * TPT;
   if (n <= 0 || wg_tok0 >= n) return;                // the whole workgroup: uniform
   const bool bad_len = n > L || (int64_t)L > (int64_t)max_blocks * BS;
 
   const int g = lane >> 4, c = lane & 15;
-  const int tok0 = wg_tok0 + wave * TPT;
+  const int tok0 = wg_tok0 + wave * TW * TPT;          // first token of the wave's tiles
   const bool active = tok0 < n && !bad_len;
-  const int my_tok = tok0 + c / G;
-  const bool row_live = my_tok < n;
-  MfmaState<D> st;
-  mfma_begin_row<Kv16, D>(st, query, (int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G, row_live,
-                          g);
   // scores are scaled after the max (one multiply per row instead of one per
   // score), which needs a non-negative scale: a negative one moves its sign
   // into the query (exact)
-  if (qk_scale < 0.f) {
+  const uint32_t q_sign = qk_scale < 0.f ? 0x80008000u : 0u;
+  qk_scale = fabsf(qk_scale);
+  MfmaState<D> st[TW];
+  f32x4 acc_l[TW];                                    // row sums of the rounded weights, rows as acc
+  int row_last[TW];                                   // last visible key of this lane's row l%16, per tile
 #pragma unroll
-    for (int k = 0; k < KS; ++k) st.qb[k] ^= 0x80008000u;
-    qk_scale = -qk_scale;
+  for (int t = 0; t < TW; ++t) {
+    const int my_tok = tok0 + t * TPT + c / G;
+    const bool row_live = my_tok < n;
+    mfma_begin_row<Kv16, D>(st[t], query, (int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G,
+                            row_live, g);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) st[t].qb[k] ^= q_sign;
+    acc_l[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    row_last[t] = L - n + min(my_tok, n - 1);
   }
-  f32x4 acc_l = {0.f, 0.f, 0.f, 0.f};                // row sums of the rounded weights, rows as acc
   const u32x4 ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
   const float inf = opaque_inf();
-  const int my_first = L - n + tok0, my_last = L - n + min(tok0 + TPT, n) - 1;
+  const int my_first = L - n + tok0, my_last = L - n + min(tok0 + TW * TPT, n) - 1;
   const int my_b_end = active ? my_last / BS + 1 : 0;
   const int my_p_end = (my_b_end + 1) / 2;            // block pairs this wave consumes
   const int my_p_open = ((my_first + 1) / BS) / 2;    // pairs before this one are visible to every row
-  const int row_last = L - n + min(my_tok, n - 1);
-  const int wg_last = L - n + min(wg_tok0 + 8 * TPT, n) - 1;
+  const int wg_last = L - n + min(wg_tok0 + 8 * TW * TPT, n) - 1;
   const int wg_b_end = bad_len ? 0 : wg_last / BS + 1;
   const int* bt_row = block_tables + (int64_t)s * max_blocks;
 
-  // staging role of this wave: block `sblk` of every stage, K or V
+  // staging role of this wave: blocks sblk + 4j of every stage, K or V
   const bool v_role = wave >= 4;
   const int sblk = wave & 3;
   const int row_stride = num_kv_heads * D * KVB;
   const int blk_bytes = BS * row_stride;
   const int head_off = kvh * D * KVB;
   const char* pool = v_role ? v_cache : k_cache;
-  const bool v_lane = lane < VL;
-  int voff[4];
+  int voff[KC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!v_role) {
-      const int q = lane + 64 * (i % KC);             // K chunk: row q / CPR, column q % CPR
-      voff[i] = (q / CPR) * row_stride + head_off + (q % CPR) * 16;
-    } else {                                          // V: key 4*quad + i, column lane % CPR
-      voff[i] = (4 * (lane / CPR) + i) * row_stride + head_off + (lane % CPR) * 16;
-    }
+  for (int i = 0; i < KC; ++i) {
+    const int q = lane + 64 * i;                      // chunk: row q / CPR, column q % CPR
+    voff[i] = (q / CPR) * row_stride + head_off + (q % CPR) * 16;
   }
 
-  u32x4 regs[4];
+  u32x4 regs[SBW][KC];
   int ids = 0;                                        // block ids of the current window of 64 blocks
   bool bad_id = false;
   auto issue = [&](int stage) {
-    const int bi = stage * kPfStageBlocks + sblk;
-    if ((stage & 15) == 0) {                          // stage * 4 is a multiple of 64: a new window
+    if ((stage & (64 / kPfStageBlocks - 1)) == 0) {   // the stage starts a new window
       const int idx = stage * kPfStageBlocks + lane;
       ids = idx < wg_b_end ? bt_row[idx] : 0;
       bad_id |= __ballot(idx < wg_b_end && (unsigned)ids >= (unsigned)num_blocks) != 0;
     }
-    const int id = __builtin_amdgcn_readlane(ids, bi & 63);
-    const bool ok = bi < wg_b_end && (unsigned)id < (unsigned)num_blocks;
-    const int rows = ok ? min(BS, L - bi * BS) : 0;
-    const __amdgpu_buffer_rsrc_t r = block_rsrc(pool + (int64_t)(ok ? id : 0) * blk_bytes, rows * row_stride);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (v_role ? v_lane : i < KC) regs[i] = load16<NT>(r, voff[i], 0);
+    for (int j = 0; j < SBW; ++j) {
+      const int bi = stage * kPfStageBlocks + sblk + 4 * j;
+      const int id = __builtin_amdgcn_readlane(ids, bi & 63);
+      const bool ok = bi < wg_b_end && (unsigned)id < (unsigned)num_blocks;
+      const int rows = ok ? min(BS, L - bi * BS) : 0;
+      const __amdgpu_buffer_rsrc_t r = block_rsrc(pool + (int64_t)(ok ? id : 0) * blk_bytes, rows * row_stride);
+#pragma unroll
+      for (int i = 0; i < KC; ++i) regs[j][i] = load16<NT>(r, voff[i], 0);
+    }
   };
   // word w (elements 2w, 2w+1) of a staged chunk as 16-bit elements
   auto word = [&](const u32x4& x, int w) -> uint32_t {
@@ -865,83 +879,131 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
     else return (w & 1) ? fp8x2_to<E, true>(x[w >> 1]) : fp8x2_to<E, false>(x[w >> 1]);
   };
   auto commit = [&](int buf) {
-    char* sb = smem + buf * SB;
-    if (!v_role) {
+    char* sb = smem + buf * SB + (v_role ? KB : 0);
+#pragma unroll
+    for (int j = 0; j < SBW; ++j)
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
         const int q = lane + 64 * i;
-        char* dst = sb + (sblk * BS + q / CPR) * RP + (q % CPR) * DPC * 2;
+        char* dst = sb + ((sblk + 4 * j) * BS + q / CPR) * (v_role ? VP : RP) + (q % CPR) * DPC * 2;
+        const u32x4& x = regs[j][i];
 #pragma unroll
         for (int h = 0; h < DPC / 8; ++h)
           *reinterpret_cast<u32x4*>(dst + 16 * h) =
-              u32x4{word(regs[i], 4 * h), word(regs[i], 4 * h + 1), word(regs[i], 4 * h + 2), word(regs[i], 4 * h + 3)};
+              u32x4{word(x, 4 * h), word(x, 4 * h + 1), word(x, 4 * h + 2), word(x, 4 * h + 3)};
       }
-    } else if (v_lane) {
-      const int col = lane % CPR;
-      char* dst = sb + KB + (sblk >> 1) * PB + (lane / CPR) * QB + (sblk & 1) * 8 + col * (DPC / VE) * 16;
+  };
+
+  // A step covers blocks 2p, 2p+1 of a stage for both tiles (key0: position
+  // of block 2p's first key), in three parts: scores (QK and the row maxima),
+  // rescale (rare: one branch for both tiles) and weights_pv (exponentials
+  // and PV).  Every row sees key 0, and the first pair is consumed before any
+  // other, so m_ref is finite whenever weights are taken.
+  // raw scores: lane l holds row l%16, keys key0 + 16*(i/4) + 4*(l/16) + i%4
+  struct Scores {
+    float z[TW][8];
+    float bm[TW];                                     // row maxima, scaled
+    bool vis[TW][8];                                  // visible keys (masked steps)
+  };
+  struct KOps { u32x4 a[KS], b[KS]; };                // K operands of blocks 2p and 2p+1
+  auto k_read = [&](const char* sbuf, int p, KOps& x) {
+    const char* ka = sbuf + 2 * p * BS * RP + c * RP + 16 * g;
 #pragma unroll
-      for (int w = 0; w < DPC / 2; ++w) {
-        const uint32_t k0 = word(regs[0], w), k1 = word(regs[1], w), k2 = word(regs[2], w), k3 = word(regs[3], w);
+    for (int k = 0; k < KS; ++k) {
+      x.a[k] = *reinterpret_cast<const u32x4*>(ka + 64 * k);
+      x.b[k] = *reinterpret_cast<const u32x4*>(ka + BS * RP + 64 * k);
+    }
+  };
+  // B operand of output columns d = 16T + c: V rows 4g..4g+3 of both blocks
+  auto v_read = [&](const char* sbuf, int p, u32x4* vb) {
+    const char* va = sbuf + KB + (2 * p * BS + 4 * g + (c >> 2)) * VP + 8 * (c & 3);
 #pragma unroll
-        for (int hi = 0; hi < 2; ++hi) {
-          const int e = 2 * w + hi;                   // element of the chunk: d = col * DPC + e
-          const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-          *reinterpret_cast<u32x2*>(dst + ((e % VE) * 16 + e / VE) * 16) =
-              u32x2{__builtin_amdgcn_perm(k1, k0, sel), __builtin_amdgcn_perm(k3, k2, sel)};
-        }
+    for (int T = 0; T < VE; ++T) {
+      const u32x2 x = lds_read_tr16(va + 32 * T), y = lds_read_tr16(va + BS * VP + 32 * T);
+      vb[T] = u32x4{x[0], x[1], y[0], y[1]};
+    }
+  };
+  auto qk = [&](int t, const KOps& x, Scores& r) {
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      sa = M::qk(x.a[k], st[t].qb[k], sa);
+      sb = M::qk(x.b[k], st[t].qb[k], sb);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.z[t][i] = sa[i];
+      r.z[t][4 + i] = sb[i];
+    }
+  };
+  auto maxima = [&](auto masked_tag, int t, int key0, Scores& r) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r.vis[t][i] = !MASKED || key0 + 16 * (i >> 2) + 4 * g + (i & 3) <= row_last[t];
+      if (MASKED && !r.vis[t][i]) r.z[t][i] = -INFINITY;
+    }
+    const float zm =
+        max_nonan(max_nonan(max_nonan(r.z[t][0], r.z[t][1], inf), max_nonan(r.z[t][2], r.z[t][3], inf), inf),
+                  max_nonan(max_nonan(r.z[t][4], r.z[t][5], inf), max_nonan(r.z[t][6], r.z[t][7], inf), inf), inf);
+    r.bm[t] = rows_max_nonan(zm, inf) * qk_scale;
+  };
+  auto rescale = [&](const Scores& r) {
+    bool up[TW], any = false;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      up[t] = r.bm[t] > st[t].m_ref + kRescaleThreshold;
+      any = any || up[t];
+    }
+    if (__ballot(any)) {
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        if (!__ballot(up[t])) continue;
+        const float m_new = fmaxf(st[t].m_ref, r.bm[t]);
+        const float alpha = __builtin_amdgcn_exp2f(st[t].m_ref - m_new);   // 0 on the first pair
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int T = 0; T < VE; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[t].acc[T][i] *= ar[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_l[t][i] *= ar[i];
+        st[t].m_ref = m_new;
       }
     }
   };
-
-  // Blocks 2p, 2p+1 of a stage; key0: position of block 2p's first key.
-  // Every row sees key 0, and the first pair is consumed before any other,
-  // so m_ref is finite whenever weights are taken.
-  auto consume = [&](auto masked_tag, const char* sb, int p, int key0) {
+  auto weights = [&](auto masked_tag, int t, const Scores& r) -> u32x4 {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const char* ka = sb + 2 * p * BS * RP + c * RP + 16 * g;
-    const char* kb = ka + BS * RP;
-    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sbk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      sa = M::qk(*reinterpret_cast<const u32x4*>(ka + 64 * k), st.qb[k], sa);
-      sbk = M::qk(*reinterpret_cast<const u32x4*>(kb + 64 * k), st.qb[k], sbk);
-    }
-    // lane l holds raw scores of row l%16, keys key0 + 16*(i/4) + 4*(l/16) + i%4
-    float z[8] = {sa[0], sa[1], sa[2], sa[3], sbk[0], sbk[1], sbk[2], sbk[3]};
-    bool vis[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      vis[i] = !MASKED || key0 + 16 * (i >> 2) + 4 * g + (i & 3) <= row_last;
-      if (MASKED && !vis[i]) z[i] = -INFINITY;
-    }
-    const float zm = max_nonan(max_nonan(max_nonan(z[0], z[1], inf), max_nonan(z[2], z[3], inf), inf),
-                               max_nonan(max_nonan(z[4], z[5], inf), max_nonan(z[6], z[7], inf), inf), inf);
-    const float bm = rows_max_nonan(zm, inf) * qk_scale;
-    if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
-      const float m_new = fmaxf(st.m_ref, bm);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);     // 0 on the first pair
-      float ar[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int T = 0; T < VE; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.acc[T][i] *= ar[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc_l[i] *= ar[i];
-      st.m_ref = m_new;
-    }
     float p8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float t = fmaf(z[i], qk_scale, -st.m_ref);
-      p8[i] = __builtin_amdgcn_exp2f(MASKED && !vis[i] ? -INFINITY : t);
+      const float e = fmaf(r.z[t][i], qk_scale, -st[t].m_ref);
+      p8[i] = __builtin_amdgcn_exp2f(MASKED && !r.vis[t][i] ? -INFINITY : e);
     }
-    const u32x4 pa = {pack2<E>(p8[0], p8[1]), pack2<E>(p8[2], p8[3]), pack2<E>(p8[4], p8[5]), pack2<E>(p8[6], p8[7])};
-    const char* vb = sb + KB + p * PB + g * QB + c * 16;
+    return u32x4{pack2<E>(p8[0], p8[1]), pack2<E>(p8[2], p8[3]), pack2<E>(p8[4], p8[5]), pack2<E>(p8[6], p8[7])};
+  };
+  auto pv = [&](int t, const u32x4& pa, const u32x4* vb) {
 #pragma unroll
-    for (int T = 0; T < VE; ++T) st.acc[T] = M::qk(pa, *reinterpret_cast<const u32x4*>(vb + 256 * T), st.acc[T]);
-    acc_l = M::qk(pa, ones, acc_l);
+    for (int T = 0; T < VE; ++T) st[t].acc[T] = M::qk(pa, vb[T], st[t].acc[T]);
+    acc_l[t] = M::qk(pa, ones, acc_l[t]);
+  };
+  // one step over a pair, not pipelined
+  auto step = [&](auto masked_tag, const char* sbuf, int p, int key0) {
+    Scores r;
+    KOps x;
+    k_read(sbuf, p, x);
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      qk(t, x, r);
+      maxima(masked_tag, t, key0, r);
+    }
+    rescale(r);
+    u32x4 vb[VE];
+    v_read(sbuf, p, vb);
+#pragma unroll
+    for (int t = 0; t < TW; ++t) pv(t, weights(masked_tag, t, r), vb);
   };
 
   const int stages = (wg_b_end + kPfStageBlocks - 1) / kPfStageBlocks;
@@ -953,27 +1015,68 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   __syncthreads();
   for (int stg = 0; stg < stages; ++stg) {
     if (stg + 1 < stages) issue(stg + 1);
-    const char* sb = smem + (stg & 1) * SB;
-    const int p_lo = 2 * stg, p_hi = min(p_lo + 2, my_p_end), p_mid = min(max(my_p_open, p_lo), p_hi);
+    const char* sbuf = smem + (stg & 1) * SB;
+    const int p_lo = stg * (kPfStageBlocks / 2), p_hi = min(p_lo + kPfStageBlocks / 2, my_p_end);
+    const int p_mid = min(max(my_p_open, p_lo), p_hi);
+    // pairs every row sees, software-pipelined: the exponentials and PV of
+    // one pair and the QK and maxima of the next form one scheduling region,
+    // ordered so that each group of vector instructions has matrix-core work
+    // of the other tile or pair beside it
+    if (p_lo < p_mid) {
+      Scores cur;
+      {
+        KOps x;
+        k_read(sbuf, 0, x);
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          qk(t, x, cur);
+          maxima(std::false_type{}, t, 0, cur);
+        }
+      }
 #pragma unroll 1
-    for (int p = p_lo; p < p_mid; ++p) consume(std::false_type{}, sb, p - p_lo, p * 2 * BS);
+      for (int p = p_lo; p + 1 < p_mid; ++p) {
+        rescale(cur);
+        Scores nxt;
+        KOps x;
+        u32x4 vb[VE];
+        v_read(sbuf, p - p_lo, vb);
+        k_read(sbuf, p + 1 - p_lo, x);
+        const u32x4 pa0 = weights(std::false_type{}, 0, cur);
+        qk(0, x, nxt);
+        pv(0, pa0, vb);
+        const u32x4 pa1 = weights(std::false_type{}, 1, cur);
+        qk(1, x, nxt);
+        maxima(std::false_type{}, 0, 0, nxt);
+        pv(1, pa1, vb);
+        maxima(std::false_type{}, 1, 0, nxt);
+        cur = nxt;
+      }
+      rescale(cur);
+      u32x4 vb[VE];
+      v_read(sbuf, p_mid - 1 - p_lo, vb);
+#pragma unroll
+      for (int t = 0; t < TW; ++t) pv(t, weights(std::false_type{}, t, cur), vb);
+    }
+    // pairs on the causal diagonal
 #pragma unroll 1
-    for (int p = p_mid; p < p_hi; ++p) consume(std::true_type{}, sb, p - p_lo, p * 2 * BS);
+    for (int p = p_mid; p < p_hi; ++p) step(std::true_type{}, sbuf, p - p_lo, p * 2 * BS);
     if (stg + 1 < stages) commit((stg + 1) & 1);
     __syncthreads();
   }
   const bool bad = bad_len || __syncthreads_or(bad_id);
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;                          // rows r of the accumulators: token tok0 + r/G, head r%G
-    const int tok = tok0 + r / G;
-    if (tok >= n) continue;
-    const float inv = acc_l[i] > 0.f ? v_scale / acc_l[i] : 0.f;
-    float o[VE];
+  for (int t = 0; t < TW; ++t) {
 #pragma unroll
-    for (int T = 0; T < VE; ++T) o[T] = bad ? qnan() : st.acc[T][i] * inv;
-    store_run<E, VE>(out, ((int64_t)(q0 + tok) * num_heads + kvh * G + r % G) * D + VE * c, o);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;                        // rows r of the accumulators: token r/G of the tile, head r%G
+      const int tok = tok0 + t * TPT + r / G;
+      if (tok >= n) continue;
+      const float inv = acc_l[t][i] > 0.f ? v_scale / acc_l[t][i] : 0.f;
+      const int64_t o0 = ((int64_t)(q0 + tok) * num_heads + kvh * G + r % G) * D + c;
+#pragma unroll
+      for (int T = 0; T < VE; ++T) store_elem<E>(out, o0 + 16 * T, bad ? qnan() : st[t].acc[T][i] * inv);
+    }
   }
 }
 

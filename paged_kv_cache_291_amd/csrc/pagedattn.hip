@@ -340,8 +340,8 @@ int launch_prefill(void* out, const void* query, const void* kc, const void* vc,
                    hipStream_t st) {
   const int tiles = ceil_div(max_query_len * G, 16);
   if (tiles >= kPrefillLdsTiles) {
-    // many query tiles per (sequence, kv head): 8 tiles per workgroup share K/V through LDS
-    const int gpp = ceil_div(tiles, 8);
+    // many query tiles per (sequence, kv head): the tiles of a workgroup share K/V through LDS
+    const int gpp = ceil_div(tiles, 8 * kPfTilesPerWave);
     const long long pairs = (long long)num_seqs * num_kv_heads;
     const long long grid = (pairs + 7) / 8 * 8 * gpp;
     if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
