@@ -30,14 +30,15 @@ def _case(seed, Hq, Hkv, D, dtype, lens=LENS, nq=NQ):
     return wl, starts, q
 
 
-def _gpu(wl, starts, q, kc=None, vc=None, fp8=None, max_q=0, bt=None, sl=None):
+def _gpu(wl, starts, q, kc=None, vc=None, fp8=None, max_q=0, bt=None, sl=None, scale=None):
     out = torch.empty_like(q, device="cuda")
     kw = {} if fp8 is None else dict(k_scale=fp8[0], v_scale=fp8[1])
     P.paged_attention_prefill(out, q.cuda(), (kc if kc is not None else wl.k_cache).cuda(),
                               (vc if vc is not None else wl.v_cache).cuda(),
                               torch.from_numpy(wl.block_tables if bt is None else bt).cuda(),
                               torch.from_numpy(wl.seq_lens if sl is None else sl).cuda(),
-                              torch.from_numpy(starts).cuda(), wl.scale, max_query_len=max_q, **kw)
+                              torch.from_numpy(starts).cuda(), wl.scale if scale is None else scale,
+                              max_query_len=max_q, **kw)
     torch.cuda.synchronize()
     return out.cpu().double().numpy()
 
@@ -71,6 +72,23 @@ def test_prefill_fp8_pools(Hq, Hkv):
     print(f"prefill fp8 {Hq}/{Hkv}: max-abs {diff.max():.3e}", flush=True)
     assert np.isfinite(g).all()
     assert float(np.max(diff - (TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref)))) <= 0.0
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0])
+@pytest.mark.parametrize("lens,nq", [([300, 40, 64, 17], [64, 40, 17, 3]),     # 64 tokens x 4 heads: 16 tiles
+                                     ([300, 40, 64, 17], [4, 3, 1, 4])])      # <= 16 rows: balanced split
+def test_prefill_non_positive_scale(scale, lens, nq):
+    """The many-tile kernel scales scores after the row maximum, so a negative
+    scale moves its sign into the query, and a zero one gives equal weights
+    over the visible keys."""
+    wl, starts, q = _case(91, 32, 8, 128, "bf16", lens, nq)
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                   wl.block_tables, wl.seq_lens, starts, scale, "bf16")
+    g = _gpu(wl, starts, q, scale=scale)
+    d = np.abs(g - ref)
+    print(f"prefill scale {scale} max_q={max(nq)}: max-abs {d.max():.3e}", flush=True)
+    assert np.isfinite(g).all()
+    assert float(np.max(d - (TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref)))) <= 0.0
 
 
 def test_prefill_contract_violations_give_nan_rows():
