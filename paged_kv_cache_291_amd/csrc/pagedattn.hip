@@ -32,7 +32,7 @@ constexpr int kSkWorkgroups = 256;
 // Largest batch the balanced split handles (its prefix sums live in LDS).
 constexpr int kSkMaxSeqs = 16383;
 // Multi-token queries: from this many 16-row query tiles per (sequence, kv
-// head) on, workgroups of 8 tiles share each K/V block through LDS.
+// head) on, the tiles share each K/V block through LDS (16 per workgroup).
 constexpr int kPrefillLdsTiles = 4;
 
 // ------------------------------------------------------------ scatter kernel
@@ -152,6 +152,14 @@ size_t balanced_mq_workspace_bytes(int num_seqs, int num_kv_heads, int head_size
          (size_t)kSkWorkgroups * num_kv_heads * 2 * 16 * (head_size + kRecHead) * sizeof(float);
 }
 
+// Rows per wave of the balanced-split merges: four (16 lanes each) when the
+// batch has enough sequences that each row has few records, else one.  Long
+// contexts over few sequences leave dozens of records per row, which a whole
+// wave reads 16 at a time (8 x 32k tokens: 5.7 us with one row per wave,
+// about twice that with four).
+constexpr int kMergeQuadMinSeqs = 64;
+int merge_rows_per_wave(int num_seqs) { return num_seqs >= kMergeQuadMinSeqs ? 4 : 1; }
+
 // Largest divisor of num_kv_heads that is at most 8: kv heads per workgroup.
 int heads_per_workgroup(int num_kv_heads) {
   for (int d = 8; d > 1; --d)
@@ -194,8 +202,12 @@ int launch_mfma(const Args& a, hipStream_t st) {
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_seqs, a.num_heads, a.num_kv_heads, a.max_blocks,
                      a.num_blocks, a.qk_scale, a.v_scale, hpw, nwg, ws_seq, ws_rec);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  hipLaunchKernelGGL((pa_sk_merge_kernel<E, D, G>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
-                     a.out, ws_seq, ws_rec, a.num_heads, hpw, nwg);
+  if (merge_rows_per_wave(a.num_seqs) == 4)
+    hipLaunchKernelGGL((pa_sk_merge_kernel<E, D, G, 4>), dim3((unsigned)(a.num_seqs * ceil_div(a.num_heads, 4))),
+                       dim3(64), 0, st, a.out, ws_seq, ws_rec, a.num_heads, hpw, nwg);
+  else
+    hipLaunchKernelGGL((pa_sk_merge_kernel<E, D, G, 1>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
+                       a.out, ws_seq, ws_rec, a.num_heads, hpw, nwg);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -388,9 +400,10 @@ int launch_mq_split(void* out, const void* query, const void* kc, const void* vc
                      static_cast<const char*>(kc), static_cast<const char*>(vc), bt, sl, num_seqs, num_heads,
                      num_kv_heads, max_blocks, num_blocks, qk_scale, v_scale, hpw, nwg, ws_seq, ws_rec, qs);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  const long long grid = (long long)num_seqs * max_q * num_heads;
-  hipLaunchKernelGGL((pa_sk_merge_mq_kernel<E, D, G>), dim3((unsigned)grid), dim3(64), 0, st, out, ws_seq, ws_rec,
-                     qs, num_heads, hpw, nwg, max_q);
+  const int rpw = merge_rows_per_wave(num_seqs);
+  const long long grid = (long long)num_seqs * num_kv_heads * ceil_div(max_q * G, rpw);
+  auto mk = rpw == 4 ? pa_sk_merge_mq_kernel<E, D, G, 4> : pa_sk_merge_mq_kernel<E, D, G, 1>;
+  hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(64), 0, st, out, ws_seq, ws_rec, qs, num_heads, hpw, nwg, max_q);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -118,10 +118,13 @@ def test_repeat_runs_bit_identical(ps):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 32, 8), ("f16", 12, 12), ("bf16", 8, 2), ("bf16", 16, 16)])
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 32, 8), ("f16", 12, 12), ("bf16", 8, 2), ("bf16", 16, 16),
+                                           ("bf16", 2, 1), ("f16", 6, 3)])
 def test_many_short_sequences(dtype, Hq, Hkv):
     """Hundreds of short sequences (many per workgroup range, empty ones
-    between them, more sequences than threads in the prefix-sum pass)."""
+    between them, more sequences than threads in the prefix-sum pass); the
+    merge then takes four heads per wave, including head counts that are not
+    a multiple of four."""
     rng = np.random.default_rng(Hq * 100 + Hkv)
     lens = rng.integers(0, 70, size=700)
     lens[::37] = 0
