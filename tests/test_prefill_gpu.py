@@ -60,6 +60,36 @@ def test_prefill_sweep(dtype, D, Hq, Hkv):
         assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
 
 
+# Query counts around the many-tile kernel's unit of work (2 tiles per wave,
+# 16 per workgroup): with G = 8 a tile is 2 tokens, so n = 8 is the smallest
+# batch it takes (4 tiles), 32 fills one workgroup and 33 starts a second
+# whose first wave has one token; cached prefixes from 0 to 101 tokens put the
+# causal diagonal at many offsets inside a block pair.
+LDS_LENS = [8, 10, 46, 48, 65, 33, 64, 165, 40, 31, 129, 200]
+LDS_NQ = [8, 9, 31, 32, 33, 33, 63, 64, 24, 16, 65, 100]
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,fp8", [("bf16", 128, 16, 2, False), ("f16", 64, 16, 2, False),
+                                                ("bf16", 128, 32, 8, True), ("f16", 64, 8, 1, True)])
+def test_many_tile_kernel_edges(dtype, D, Hq, Hkv, fp8):
+    seed = zlib.crc32(f"lds-{dtype}-{D}-{Hq}-{Hkv}-{fp8}".encode()) % 10000
+    wl, starts, q = _case(seed, Hq, Hkv, D, dtype, LDS_LENS, LDS_NQ)
+    if fp8:
+        kc8, vc8 = W.with_fp8_pools(wl, seed)
+        ks, vs = 1.0 / 128, 1.0 / 96
+        g = _gpu(wl, starts, q, kc8, vc8, fp8=(ks, vs))
+        ref = oracle.paged_prefill_ref(W.raw_numpy(q), kc8.numpy(), vc8.numpy(), wl.block_tables, wl.seq_lens,
+                                       starts, wl.scale, dtype, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    else:
+        g = _gpu(wl, starts, q)
+        ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                       wl.block_tables, wl.seq_lens, starts, wl.scale, dtype)
+    diff = np.abs(g - ref)
+    print(f"many-tile {dtype} D={D} {Hq}/{Hkv} fp8={fp8}: max-abs {diff.max():.3e}", flush=True)
+    assert np.isfinite(g).all()
+    assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8)])
 def test_prefill_fp8_pools(Hq, Hkv):
     wl, starts, q = _case(600 + Hq, Hq, Hkv, 128, "bf16")
