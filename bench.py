@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -70,12 +71,20 @@ def parse():
     return ap.parse_args()
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without comments and with runs of white space collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of every kernel source file: counter results are tied to it."""
+    """Hash of the code of every kernel source file (comments and layout
+    excluded): counter results are tied to it."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SRC_DIR)):
         h.update(name.encode())
-        h.update(open(os.path.join(KERNEL_SRC_DIR, name), "rb").read())
+        h.update(code_only(open(os.path.join(KERNEL_SRC_DIR, name)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -161,7 +161,8 @@ int paged_attention_decode(void* out, const void* query, const void* k_cache, co
  * verification: each kv head's query rows fit one 16-row tile) and num_seqs
  * <= 16383, the batch's blocks are split evenly over the GPU as in decode and
  * a second kernel merges partial results (needs the workspace); otherwise one
- * wave per 16-row tile, 8 tiles sharing K/V through LDS when there are many.
+ * wave per 16-row tile, or, when there are many, two tiles per wave and 16
+ * per workgroup sharing K/V through LDS.
  * Rows of a sequence with n_s > seq_lens[s], a length past its table row or a
  * block id outside the pool are NaN.  Rows beyond max_query_len are not
  * written.

@@ -762,9 +762,8 @@ constexpr int kPfTilesPerWave = 2;
 // tiles); wave w owns tiles 16*grp + 2w and 2w + 1 (16 (token, head) rows
 // each, as in pa_prefill_kernel).  The workgroup streams the sequence's
 // blocks in stages of kPfStageBlocks, double-buffered in LDS with one barrier
-// per stage: wave w copies blocks w%4 and w%4 + 4 of the next stage, K
-// (w < 4) or V (w >= 4), while every wave consumes the current stage's blocks
-// it can see,
+// per stage: wave w copies blocks w%4 + 4j of the next stage, K (w < 4) or V
+// (w >= 4), while every wave consumes the current stage's blocks it can see,
 // two blocks per step, both of its tiles on each operand read from LDS:
 //   QK: two 16-key score tiles (16x16x32 MFMAs over head_size);
 //   PV: one 16x16x32 MFMA per 16 output columns over the pair's 32 keys, and
