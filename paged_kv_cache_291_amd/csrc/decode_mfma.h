@@ -637,6 +637,13 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
   }
   int s = lo;
   float* rec_wg = ws_rec + ((int64_t)blockIdx.x * 2 * hpw + wave) * RPW * REC;
+  // MQ: the record of a first segment that ends inside the range is held in
+  // registers and written after the range's last segment.  Records of many
+  // rows add up to more dirty lines than an XCD's L2 holds; written early,
+  // they are flushed to HBM in the middle of the K/V stream.
+  MfmaState<D> held;
+  bool held_bad = false, have_held = false;
+  int held_a = 0, held_nq = 0;
   for (int u = u0; u < u1;) {
     const int c0 = s_cum[s], c1 = s_cum[s + 1];
     if (c1 == c0) { ++s; continue; }
@@ -658,7 +665,15 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
           bad = mfma_segment_rows<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
                                                       b0, b1, (L - nq + 1) / BS, row_last, L - 1, num_blocks,
                                                       num_kv_heads, kvh, qk_scale, lane);
-        mfma_finish_rows<E, D, G>(st, bad, out, a, nq, num_heads, kvh, rec, REC, v_scale, lane);
+        if (u == u0 && rec != nullptr && c1 < u1) {     // first segment, not the range's last
+          held = st;
+          held_bad = bad;
+          held_a = a;
+          held_nq = nq;
+          have_held = true;
+        } else {
+          mfma_finish_rows<E, D, G>(st, bad, out, a, nq, num_heads, kvh, rec, REC, v_scale, lane);
+        }
       }
     } else {
       const int64_t row0 = (int64_t)s * num_heads + kvh * G;
@@ -671,6 +686,10 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     }
     u += b1 - b0;
     ++s;
+  }
+  if constexpr (MQ) {
+    if (have_held)
+      mfma_finish_rows<E, D, G>(held, held_bad, out, held_a, held_nq, num_heads, kvh, rec_wg, REC, v_scale, lane);
   }
 }
 
