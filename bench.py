@@ -166,8 +166,9 @@ def write_traffic(args):
 
 
 def cpu_baseline(wl, seconds: float, gpu_out, fp8_pools=None):
-    """Time the oracle (single thread) on the first sequences of the workload
-    (over the fp8 code pools when given)."""
+    """Time the oracle (single thread) on the workload's sequences in order
+    (over the fp8 code pools when given) until ``seconds`` of oracle time are
+    spent; a batch that takes less is walked again from its first sequence."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -179,25 +180,30 @@ def cpu_baseline(wl, seconds: float, gpu_out, fp8_pools=None):
     if fp8_pools is not None:
         kc, vc = fp8_pools[0].numpy(), fp8_pools[1].numpy()
         extra = dict(kv_dtype="e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    S = wl.num_seqs
     done, tok, elapsed, err = 0, 0, 0.0, 0.0
     with threadpool_limits(1):
-        while done < wl.num_seqs and elapsed < seconds:
+        while elapsed < seconds and done < 64 * S:
+            s = done % S
             t0 = time.perf_counter()
             ref = oracle.paged_decode_ref(q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale, wl.dtype,
-                                          seqs=[done], **extra)
+                                          seqs=[s], **extra)
             elapsed += time.perf_counter() - t0
-            g = gpu_out[done].double().numpy()
-            err = max(err, float(np.max(np.abs(g - ref[0]))))
-            tok += int(wl.seq_lens[done])
+            if done < S:
+                g = gpu_out[s].double().numpy()
+                err = max(err, float(np.max(np.abs(g - ref[0]))))
+            tok += int(wl.seq_lens[s])
             done += 1
     kv = tok * wl.num_kv_heads * wl.head_size * 2 * (1 if fp8_pools is not None else W.ELEM_BYTES[wl.dtype])
+    walked = (f"first {done} of {S} sequences" if done <= S else
+              f"{done // S} passes over all {S} sequences" + (f" and the first {done % S} again" if done % S else ""))
     return {
         "value": round(kv / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {done} of {wl.num_seqs} sequences ({tok} tokens, {kv} KV bytes) of the same "
-                  f"workload, float64 NumPy, one thread, {elapsed:.2f} s",
+        "sample": f"{walked} ({tok} tokens, {kv} KV bytes) of the same workload, float64 NumPy, "
+                  f"one thread, {elapsed:.2f} s",
     }, err
 
 
