@@ -181,12 +181,21 @@ template <class E, class KV, int D, int G, bool NT>
 int launch_mfma(const Args& a, hipStream_t st) {
   if (a.part_tokens > 0) {
     const int hpw = heads_per_workgroup(a.num_kv_heads);
-    const long long grid = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
-    if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    const long long items = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
+    if (items > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    const int groups = a.num_kv_heads / hpw;
+    // Up to two items per CU: one round of at most one workgroup per CU,
+    // workgroup b taking items b and b + grid (grid a multiple of the head
+    // groups, so both are of its head group), the first item's record held
+    // until the second has streamed.  More items: one per workgroup, and the
+    // dispatcher fills the CUs round by round (pairing them would leave a
+    // half-empty last round whenever the rounds are odd in number).
+    const long long wgs = kSkWorkgroups >= groups ? kSkWorkgroups / groups * groups : groups;
+    const long long grid = items <= 2 * wgs ? (items < wgs ? items : wgs) : items;
     float* ws = static_cast<float*>(a.ws);
     hipLaunchKernelGGL((pa_decode_mfma_kernel<E, KV, D, G, NT>), dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                        a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                       a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, hpw, ws);
+                       a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, hpw, (int)items, ws);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
                        a.out, ws, a.sl, a.num_heads, a.max_blocks, a.part_tokens, a.num_parts);
