@@ -140,6 +140,28 @@ def test_many_short_sequences(dtype, Hq, Hkv):
         assert (g[lens == 0] == 0).all()
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,max_len", [(51, 40, 40, 512), (51, 40, 40, 1024), (103, 40, 40, 512),
+                                               (200, 32, 8, 1024), (128, 32, 8, 1024)])
+def test_fixed_split_item_pairing(S, Hq, Hkv, max_len):
+    """Fixed 512-token partitions around the launch's one-round limit: with
+    5 head groups (40 kv heads) 255 items run one per workgroup, 510 run two
+    per workgroup (a record held across items), 515 one per workgroup again;
+    with one head group 400 items pair partly and 256 do not.  Short
+    sequences leave empty second partitions."""
+    rng = np.random.default_rng(S * 1000 + Hkv + max_len)
+    lens = rng.integers(1, max_len + 1, size=S)
+    lens[0] = max_len
+    lens[1::7] = rng.integers(1, 40, size=len(lens[1::7]))
+    wl = W.make_random(S + Hkv + max_len, S, Hq, Hkv, 64, "f16", lens, pool_factor=1.1)
+    assert wl.max_seq_len == max_len
+    ref = oracle_decode(wl)
+    out, _ = gpu_decode(wl, partition_size=512)
+    _, g, diff = errors(out, ref)
+    bound = TOL["f16"] + HALF_ULP["f16"] * np.abs(ref)
+    assert np.isfinite(g).all()
+    assert float(np.max(diff - bound)) <= 0.0, float(diff.max())
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("ps", [0, 16])
 def test_contract_violations_give_nan_rows(dtype, ps):
