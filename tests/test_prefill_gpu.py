@@ -178,6 +178,30 @@ def test_few_query_rows_per_sequence(dtype, D, Hq, Hkv, fp8):
     assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 4), ("f16", 64, 8, 2), ("bf16", 16, 16, 16)])
+def test_few_rows_many_segments_per_range(dtype, Hq, Hkv, max_q):
+    """Speculative verification over hundreds of short sequences, so that a
+    workgroup's range holds several sequences: a first segment that began in
+    an earlier range and ends inside this one (its record is held until the
+    range's last segment), one that runs past the range's end as well, and
+    sequences without query rows in between.  Every row against the oracle."""
+    rng = np.random.default_rng(Hq * 10 + Hkv + max_q)
+    S = 600
+    lens = rng.integers(1, 200, size=S)
+    lens[::29] = rng.integers(400, 900, size=len(lens[::29]))   # some sequences span several ranges
+    nq = rng.integers(0, max_q + 1, size=S)
+    nq[::11] = 0
+    nq = np.minimum(nq, lens)
+    wl, starts, q = _case(700 + Hq + Hkv, Hq, Hkv, 128, dtype, lens, nq)
+    g = _gpu(wl, starts, q, max_q=max_q)
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                   wl.block_tables, wl.seq_lens, starts, wl.scale, dtype)
+    diff = np.abs(g - ref)
+    print(f"{S} short sequences {dtype} {Hq}/{Hkv} up to {max_q} rows: max-abs {diff.max():.3e}", flush=True)
+    assert np.isfinite(g).all()
+    assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
+
+
 def test_verify_8b_batch_full_size():
     """Speculative verification on the 8B-shaped batch (4 query rows per
     sequence): the balanced split with causal rows, sampled rows against
