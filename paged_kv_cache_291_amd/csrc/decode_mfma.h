@@ -464,8 +464,8 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
   bool held_bad = false, have_held = false;
   float* held_rec = nullptr;
   int64_t held_row0 = 0;
-  for (int item = blockIdx.x; item < num_items; item += gridDim.x) {
-    int w = item;
+  for (int64_t item = blockIdx.x; item < num_items; item += gridDim.x) {   // 64-bit: item + grid may pass 2^31
+    int w = (int)item;
     const int kvh = (w % groups) * hpw + (int)(threadIdx.x >> 6);
     w /= groups;
     const int part = w % num_parts;
