@@ -460,7 +460,7 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int groups = num_kv_heads / hpw;
   const int64_t cap = min((int64_t)max_blocks * BS, (int64_t)num_parts * part_tokens);
 
-  MfmaState<D> held;                          // the last item's record, not yet written
+  MfmaState<D> held;                          // the previous item's record, not yet written
   bool held_bad = false, have_held = false;
   float* held_rec = nullptr;
   int64_t held_row0 = 0;
