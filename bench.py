@@ -47,8 +47,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--op", default="decode", choices=["decode", "copy_blocks", "block_manager", "prefill"])
     ap.add_argument("--prefill-case", default="verify", choices=["verify", "chunk"],
-                    help="prefill: verify = the 8B batch with 4 query tokens per sequence (speculative "
-                         "verification); chunk = 8 sequences, 3584 cached + 512 new tokens")
+                    help="prefill: verify = the 8B batch with --query-tokens query tokens per sequence "
+                         "(speculative verification); chunk = 8 sequences, 3584 cached + 512 new tokens")
+    ap.add_argument("--query-tokens", type=int, default=4,
+                    help="prefill verify: query tokens per sequence (the speculative draft length)")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="fp8: the same workload over OCP e4m3 pools (random finite codes, scales 1/128 and 1/96)")
     ap.add_argument("--steps", type=int, default=200)
@@ -290,8 +292,9 @@ def bench_prefill(args):
     dev = torch.device("cuda:0")
     if args.prefill_case == "verify":
         wl = W.make_config(3, args.seed, poison=False)
-        nq = np.full(wl.num_seqs, 4, dtype=np.int32)
-        desc = "speculative verification on the 8B-shaped GQA batch: 256 seqs, 4 query tokens each (32/8 heads, D=128, bf16)"
+        nq = np.full(wl.num_seqs, args.query_tokens, dtype=np.int32)
+        desc = (f"speculative verification on the 8B-shaped GQA batch: 256 seqs, {args.query_tokens} query tokens each "
+                "(32/8 heads, D=128, bf16)")
     else:
         S, L, n = 8, 4096, 512
         wl = W.make_random(args.seed, S, 32, 8, 128, "bf16", [L] * S, poison=False)
@@ -337,7 +340,8 @@ def bench_prefill(args):
         "config": {"workload": desc, "query_tokens": T, "kv_bytes": kv, "flops": flops},
         "roofline": ({"bound": "hbm", "achieved": round(kv / launch / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(kv / launch / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                      "kernel": "pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel",
+                      "kernel": ("pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel"
+                                 if mq * (wl.num_heads // wl.num_kv_heads) <= 32 else "pa_prefill_lds_kernel"),
                       "bytes_per_launch": kv}
                      if args.prefill_case == "verify" else
                      {"bound": "mfma", "achieved": round(flops / launch / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

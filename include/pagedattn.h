@@ -157,12 +157,14 @@ int paged_attention_decode(void* out, const void* query, const void* k_cache, co
  *                 256-byte aligned (NULL when that size is 0); scratch, as for
  *                 paged_attention_decode
  *  other arguments as in paged_attention_decode.
- * When max_query_len * (num_heads / num_kv_heads) <= 16 (speculative
- * verification: each kv head's query rows fit one 16-row tile) and num_seqs
+ * When max_query_len * (num_heads / num_kv_heads) <= 32 (speculative
+ * verification: each kv head's query rows fit two 16-row tiles) and num_seqs
  * <= 16383, the batch's blocks are split evenly over the GPU as in decode and
- * a second kernel merges partial results (needs the workspace); otherwise one
- * wave per 16-row tile, or, when there are many, two tiles per wave and 16
- * per workgroup sharing K/V through LDS.
+ * a second kernel merges partial results (needs the workspace; with two
+ * tiles the K/V loads use the default cache policy whatever flags says,
+ * since two waves read each line); otherwise two tiles per wave and 16 per
+ * workgroup sharing K/V through LDS, or, for one tile (more than 16383
+ * sequences), one wave per tile.
  * Rows of a sequence with n_s > seq_lens[s], a length past its table row or a
  * block id outside the pool are NaN.  Rows beyond max_query_len are not
  * written.
@@ -175,8 +177,9 @@ int paged_attention_prefill(void* out, const void* query, const void* k_cache, c
                             void* stream);
 
 /* Workspace bytes paged_attention_prefill(_fp8) needs with these sizes (0:
- * none):  round_up(num_seqs * 16, 256) + 256 * num_kv_heads * 2 * 16 *
- * (head_size + 4) * 4 on the split path, else 0.  0 for invalid sizes. */
+ * none):  round_up(num_seqs * 16, 256) + 256 * num_kv_heads * 2 * 16 * tiles *
+ * (head_size + 4) * 4 on the split path, tiles = ceil(max_query_len *
+ * (num_heads / num_kv_heads) / 16), else 0.  0 for invalid sizes. */
 size_t pa_prefill_workspace_size(int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
                                  int head_size, int max_query_len);
 

@@ -598,9 +598,12 @@ __device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int n
 // A workgroup is up to 8 waves; 12 wave slots per CU would still hold only
 // one, so the register budget is that of 2 waves per SIMD.
 // MQ: several query tokens per sequence (query_start[s] .. query_start[s+1]),
-// at most 16 / G, so a wave's 16 rows are the (token, head) pairs of its kv
-// head; the sequence's final blocks are masked per row (causal), partial
-// records hold 16 rows per wave, and pa_sk_merge_mq_kernel merges them.
+// at most 16 * tiles / G; the workgroup has `tiles` waves per kv head (wave
+// = tile * hpw + head), wave (t, h) taking rows 16t .. 16t + 15 of head h's
+// (token, head) pairs.  The waves of one kv head read the same K/V rows in
+// step, so HBM sees them once.  The sequence's final blocks are masked per
+// row (causal), partial records hold 16 * tiles rows per kv head, and
+// pa_sk_merge_mq_kernel merges them.
 template <class E, class KV, int D, int G, bool NT, bool MQ = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
@@ -608,16 +611,17 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
                     const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                     int num_seqs, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
                     float qk_scale, float v_scale, int hpw, int nwg, int4* __restrict__ ws_seq,
-                    float* __restrict__ ws_rec, const int* __restrict__ query_start = nullptr) {
+                    float* __restrict__ ws_rec, const int* __restrict__ query_start = nullptr, int tiles = 1) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
-  constexpr int RPW = MQ ? 16 : G;             // record rows per wave and slot
+  const int RPK = MQ ? 16 * tiles : G;         // record rows per kv head and slot
   extern __shared__ int s_cum[];
   __shared__ int s_wsum[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hg = blockIdx.x / nwg, rank = blockIdx.x - hg * nwg;
-  const int kvh = hg * hpw + wave;
+  const int tile = wave / hpw, wv = wave - tile * hpw;   // MQ: 16-row tile of the kv head's rows
+  const int kvh = hg * hpw + wv;
 
   blocks_prefix_sum(seq_lens, num_seqs, max_blocks, s_cum, s_wsum);
   int* s_qs = s_cum + num_seqs + 1;            // MQ: query_start staged in LDS
@@ -642,7 +646,7 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     if (s_cum[s + 1] != s_cum[s]) continue;
     if (hg == 0 && tid == 0) ws_seq[s] = int4{-1, 0, 0, U};
     if constexpr (MQ) {                        // query rows of a sequence without blocks break the contract
-      const int a = s_qs[s], nq = s_qs[s + 1] - a;
+      const int a = s_qs[s], nq = tile == 0 ? s_qs[s + 1] - a : 0;
       for (int t = 0; t < nq; ++t) {
         const int64_t e0 = ((int64_t)(a + t) * num_heads + kvh * G) * D;
         for (int i = lane; i < G * D; i += 64) store_elem<E>(out, e0 + i, qnan());
@@ -662,7 +666,7 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     if (s_cum[mid] <= u0) lo = mid; else hi = mid;
   }
   int s = lo;
-  float* rec_wg = ws_rec + ((int64_t)blockIdx.x * 2 * hpw + wave) * RPW * REC;
+  float* rec_wg = ws_rec + (((int64_t)blockIdx.x * 2 * hpw + wv) * RPK + (MQ ? 16 * tile : 0)) * REC;
   // The record of a first segment that ends inside the range is held in
   // registers and written after the range's last segment: records written
   // early are flushed to HBM in the middle of the K/V stream (4 rows per
@@ -678,12 +682,14 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     const int b0 = u - c0, b1 = min(c1, u1) - c0;
     const int L = seq_lens[s];
     const bool whole = b0 == 0 && b1 == c1 - c0;
-    float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * RPW * REC);
+    float* rec = whole ? nullptr : rec_wg + (u == u0 ? 0 : (int64_t)hpw * RPK * REC);
     if constexpr (MQ) {
       const int a = s_qs[s], nq = s_qs[s + 1] - a;
       if (nq > 0) {                            // same for every wave of the workgroup
         const int g = lane >> 4, c = lane & 15;
-        const int tok = c / G;
+        const int t0 = 16 * tile / G;          // first token of this wave's tile (its rows may all be past nq:
+                                               // the wave still streams the blocks, in step with the others)
+        const int tok = t0 + c / G;
         const bool live = tok < nq;
         MfmaState<D> st;
         mfma_begin_row<KV, D>(st, query, (int64_t)(a + (live ? tok : 0)) * num_heads + kvh * G + c % G, live, g);
@@ -696,11 +702,11 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
         if (u == u0 && rec != nullptr && c1 < u1) {     // first segment, not the range's last
           held = st;
           held_bad = bad;
-          held_a = a;
-          held_nq = nq;
+          held_a = a + t0;
+          held_nq = nq - t0;
           have_held = true;
         } else {
-          mfma_finish_rows<E, D, G>(st, bad, out, a, nq, num_heads, kvh, rec, REC, v_scale, lane);
+          mfma_finish_rows<E, D, G>(st, bad, out, a + t0, nq - t0, num_heads, kvh, rec, REC, v_scale, lane);
         }
       }
     } else {

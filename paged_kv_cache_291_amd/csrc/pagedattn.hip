@@ -31,9 +31,11 @@ namespace {
 constexpr int kSkWorkgroups = 256;
 // Largest batch the balanced split handles (its prefix sums live in LDS).
 constexpr int kSkMaxSeqs = 16383;
-// Multi-token queries: from this many 16-row query tiles per (sequence, kv
-// head) on, the tiles share each K/V block through LDS (16 per workgroup).
-constexpr int kPrefillLdsTiles = 4;
+// Multi-token queries off the balanced split: from this many 16-row query
+// tiles per (sequence, kv head) on, the tiles share each K/V block through
+// LDS (16 per workgroup); one tile runs one wave per tile (8B batch, 5..8
+// tokens: 391-402 us through LDS, 608-618 us one wave per tile).
+constexpr int kPrefillLdsTiles = 2;
 
 // ------------------------------------------------------------ scatter kernel
 
@@ -146,10 +148,11 @@ size_t balanced_workspace_bytes(int num_seqs, int num_heads, int head_size) {
   return balanced_seq_bytes(num_seqs) + (size_t)kSkWorkgroups * num_heads * 2 * (head_size + kRecHead) * sizeof(float);
 }
 
-// Balanced split of multi-token queries: 16 record rows per wave instead of G.
-size_t balanced_mq_workspace_bytes(int num_seqs, int num_kv_heads, int head_size) {
+// Balanced split of multi-token queries: 16 * tiles record rows per kv head
+// instead of G.
+size_t balanced_mq_workspace_bytes(int num_seqs, int num_kv_heads, int head_size, int tiles) {
   return balanced_seq_bytes(num_seqs) +
-         (size_t)kSkWorkgroups * num_kv_heads * 2 * 16 * (head_size + kRecHead) * sizeof(float);
+         (size_t)kSkWorkgroups * num_kv_heads * 2 * 16 * tiles * (head_size + kRecHead) * sizeof(float);
 }
 
 // Rows per wave of the balanced-split merges: four (16 lanes each) when the
@@ -163,6 +166,24 @@ int merge_rows_per_wave(int num_seqs) { return num_seqs >= kMergeQuadMinSeqs ? 4
 // Largest divisor of num_kv_heads that is at most 8: kv heads per workgroup.
 int heads_per_workgroup(int num_kv_heads) {
   for (int d = 8; d > 1; --d)
+    if (num_kv_heads % d == 0) return d;
+  return 1;
+}
+
+// Multi-token queries on the balanced split: 16-row tiles per kv head (the
+// kv head's max_q * G (token, head) rows), at most kSkMaxTiles, and kv heads
+// per workgroup (a divisor of num_kv_heads, with heads * tiles <= 8 waves).
+// 8B batch, 32/8 heads: 5..8 query tokens (2 tiles) 360-370 us here against
+// 390-400 us in the LDS kernel; 12 tokens (3 tiles) 474 vs 411 us, 16 tokens
+// 577 vs 418 us, so 3 and more tiles take the LDS kernel.
+constexpr int kSkMaxTiles = 2;
+int mq_tiles(int num_heads, int num_kv_heads, int max_q) {      // kSkMaxTiles + 1: more than the split takes
+  const long long rows = (long long)max_q * (num_heads / num_kv_heads);
+  if (rows > 16LL * kSkMaxTiles) return kSkMaxTiles + 1;
+  return rows > 0 ? (int)((rows + 15) / 16) : 1;
+}
+int mq_heads_per_workgroup(int num_kv_heads, int tiles) {
+  for (int d = 8 / tiles; d > 1; --d)
     if (num_kv_heads % d == 0) return d;
   return 1;
 }
@@ -398,32 +419,39 @@ int launch_mq_split(void* out, const void* query, const void* kc, const void* vc
                     const int32_t* sl, const int32_t* qs, int num_seqs, int num_heads, int num_kv_heads,
                     int max_blocks, int num_blocks, int max_q, float qk_scale, float v_scale, bool nt, void* ws,
                     hipStream_t st) {
-  const int hpw = heads_per_workgroup(num_kv_heads);
+  const int tiles = mq_tiles(num_heads, num_kv_heads, max_q);
+  const int hpw = mq_heads_per_workgroup(num_kv_heads, tiles);
   const int groups = num_kv_heads / hpw;
   const int nwg = kSkWorkgroups / groups > 0 ? kSkWorkgroups / groups : 1;
   int4* ws_seq = static_cast<int4*>(ws);
   float* ws_rec = reinterpret_cast<float*>(static_cast<char*>(ws) + balanced_seq_bytes(num_seqs));
   const size_t lds = (size_t)2 * (num_seqs + 1) * sizeof(int);
-  auto k = nt ? pa_decode_sk_kernel<E, KV, D, G, true, true> : pa_decode_sk_kernel<E, KV, D, G, false, true>;
-  hipLaunchKernelGGL(k, dim3((unsigned)(groups * nwg)), dim3(64 * hpw), lds, st, out, query,
+  // Several tile waves read each K/V line: the default cache policy keeps it
+  // in L2 for the later ones (non-temporal loads sent them to HBM again:
+  // 8B batch, 8 query tokens, 472 -> 369 us).
+  const bool stream = nt && tiles == 1;
+  auto k = stream ? pa_decode_sk_kernel<E, KV, D, G, true, true> : pa_decode_sk_kernel<E, KV, D, G, false, true>;
+  hipLaunchKernelGGL(k, dim3((unsigned)(groups * nwg)), dim3(64 * hpw * tiles), lds, st, out, query,
                      static_cast<const char*>(kc), static_cast<const char*>(vc), bt, sl, num_seqs, num_heads,
-                     num_kv_heads, max_blocks, num_blocks, qk_scale, v_scale, hpw, nwg, ws_seq, ws_rec, qs);
+                     num_kv_heads, max_blocks, num_blocks, qk_scale, v_scale, hpw, nwg, ws_seq, ws_rec, qs, tiles);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   const int rpw = merge_rows_per_wave(num_seqs);
   const long long grid = (long long)num_seqs * num_kv_heads * ceil_div(max_q * G, rpw);
   auto mk = rpw == 4 ? pa_sk_merge_mq_kernel<E, D, G, 4> : pa_sk_merge_mq_kernel<E, D, G, 1>;
-  hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(64), 0, st, out, ws_seq, ws_rec, qs, num_heads, hpw, nwg, max_q);
+  hipLaunchKernelGGL(mk, dim3((unsigned)grid), dim3(64), 0, st, out, ws_seq, ws_rec, qs, num_heads, hpw, nwg, max_q,
+                     16 * tiles);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 // Which path a multi-token call takes, and the workspace it needs.
 bool prefill_uses_split(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
-  return max_q * (num_heads / num_kv_heads) <= 16 && num_seqs <= kSkMaxSeqs;
+  return mq_tiles(num_heads, num_kv_heads, max_q) <= kSkMaxTiles && num_seqs <= kSkMaxSeqs;
 }
 
 size_t prefill_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_size, int max_q) {
   return prefill_uses_split(num_seqs, num_heads, num_kv_heads, max_q)
-             ? balanced_mq_workspace_bytes(num_seqs, num_kv_heads, head_size) : 0;
+             ? balanced_mq_workspace_bytes(num_seqs, num_kv_heads, head_size,
+                                           mq_tiles(num_heads, num_kv_heads, max_q)) : 0;
 }
 
 int prefill_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -455,7 +483,8 @@ int prefill_impl(void* out, const void* query, const void* k_cache, const void* 
   const bool nt = (flags & PA_FLAG_SHARED_BLOCKS) == 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (prefill_uses_split(num_seqs, num_heads, num_kv_heads, mq)) {
-    const size_t need = balanced_mq_workspace_bytes(num_seqs, num_kv_heads, head_size);
+    const size_t need = balanced_mq_workspace_bytes(num_seqs, num_kv_heads, head_size,
+                                                    mq_tiles(num_heads, num_kv_heads, mq));
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PA_ERR_WORKSPACE;
 #define PA_MQ(E, KV, D, G) launch_mq_split<E, KV, D, G>(out, query, k_cache, v_cache, block_tables, seq_lens, \
     query_start, num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_blocks, mq, qks, v_scale, nt, workspace, st)

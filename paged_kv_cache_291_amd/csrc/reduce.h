@@ -232,14 +232,15 @@ pa_sk_merge_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, cons
 }
 
 // Balanced split with several query tokens per sequence (rows = (token,
-// head) pairs, 16 record rows per wave of the decode kernel): one wave per
+// head) pairs, rows_kv record rows per kv head of the decode kernel): one wave per
 // (sequence, kv head, RPW consecutive record rows).  Rows past the
 // sequence's query rows and sequences written whole by the decode kernel
 // return at once.
 template <class E, int D, int G, int RPW>
 __global__ void __launch_bounds__(64)
 pa_sk_merge_mq_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, const float* __restrict__ ws_rec,
-                      const int* __restrict__ query_start, int num_heads, int hpw, int nwg, int max_q) {
+                      const int* __restrict__ query_start, int num_heads, int hpw, int nwg, int max_q,
+                      int rows_kv) {
   constexpr int REC = rec_floats<D>();
   using MR = MergeRow<D, RPW>;
   const int per_kv = (max_q * G + RPW - 1) / RPW, num_kv = num_heads / G;
@@ -259,7 +260,7 @@ pa_sk_merge_mq_kernel(void* __restrict__ out, const int4* __restrict__ ws_seq, c
   const int first_slot = sk_range_begin(w1, U, nwg) < c0 ? 1 : 0;
   auto rec_of = [&](int j) {
     const int w = w1 + j, slot = j == 0 ? first_slot : 0;
-    return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * 16 + r) * REC;
+    return ws_rec + (int64_t)((((hg * nwg + w) * 2 + slot) * hpw + wv) * rows_kv + r) * REC;
   };
   float res[MR::kPer];
   MR::merge(rec_of, [&](int j) { return sk_range_begin(w1 + j, U, nwg) != sk_range_begin(w1 + j + 1, U, nwg); },

@@ -144,6 +144,11 @@ def test_prefill_host_errors():
     assert P.pa_prefill_workspace_size(256, 1024, 32, 8, 128, 4) == 4096 + 256 * 8 * 2 * 16 * 132 * 4
     assert P.pa_prefill_workspace_size(8, 4096, 32, 8, 128, 512) == 0
     assert P.pa_prefill_workspace_size(3, 6, 8, 8, 64, 0) == 256 + 256 * 8 * 2 * 16 * 68 * 4   # 0: T = 6 rows
+    # up to 2 tiles of 16 rows per kv head stay on the split (16 * tiles record rows per kv head)
+    assert P.pa_prefill_workspace_size(256, 2048, 32, 8, 128, 8) == 4096 + 256 * 8 * 2 * 32 * 132 * 4
+    assert P.pa_prefill_workspace_size(256, 1280, 32, 8, 128, 5) == 4096 + 256 * 8 * 2 * 32 * 132 * 4
+    assert P.pa_prefill_workspace_size(256, 2304, 32, 8, 128, 9) == 0
+    assert P.pa_prefill_workspace_size(256, 4096, 32, 8, 128, 16) == 0
 
 
 def test_python_binding_refuses_host_tensors():

@@ -178,13 +178,18 @@ def test_few_query_rows_per_sequence(dtype, D, Hq, Hkv, fp8):
     assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 4), ("f16", 64, 8, 2), ("bf16", 16, 16, 16)])
+@pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 4), ("f16", 64, 8, 2), ("bf16", 16, 16, 16),
+                                               ("bf16", 32, 8, 8), ("f16", 64, 8, 4), ("bf16", 32, 8, 16),
+                                               ("bf16", 16, 16, 48), ("f16", 8, 2, 12)])
 def test_few_rows_many_segments_per_range(dtype, Hq, Hkv, max_q):
     """Speculative verification over hundreds of short sequences, so that a
     workgroup's range holds several sequences: a first segment that began in
     an earlier range and ends inside this one (its record is held until the
     range's last segment), one that runs past the range's end as well, and
-    sequences without query rows in between.  Every row against the oracle."""
+    sequences without query rows in between.  Up to 16 rows per kv head is
+    one tile per wave; 17..32 rows take two tile waves per kv head (a wave
+    whose tile has no rows of a sequence still streams its blocks); more rows
+    go to the LDS kernel.  Every row against the oracle."""
     rng = np.random.default_rng(Hq * 10 + Hkv + max_q)
     S = 600
     lens = rng.integers(1, 200, size=S)
@@ -202,28 +207,30 @@ def test_few_rows_many_segments_per_range(dtype, Hq, Hkv, max_q):
     assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
 
 
-def test_verify_8b_batch_full_size():
-    """Speculative verification on the 8B-shaped batch (4 query rows per
-    sequence): the balanced split with causal rows, sampled rows against
-    decode over the sequence cut after each row's position."""
+@pytest.mark.parametrize("nqv", [4, 8])
+def test_verify_8b_batch_full_size(nqv):
+    """Speculative verification on the 8B-shaped batch (4 or 8 query rows per
+    sequence: one or two 16-row tiles per kv head): the balanced split with
+    causal rows, sampled rows against decode over the sequence cut after each
+    row's position."""
     wl = W.make_config(3, 0, poison=True)
     S = wl.num_seqs
-    nq = np.full(S, 4, np.int32)
+    nq = np.full(S, nqv, np.int32)
     starts = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     q = W.random_rows(3, 900, (int(starts[-1]), wl.num_heads, wl.head_size), "bf16")
-    g = _gpu(wl, starts, q, max_q=4)
+    g = _gpu(wl, starts, q, max_q=nqv)
     assert np.isfinite(g).all()
     kc, vc, qr = W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache), W.raw_numpy(q)
     worst = 0.0
     for s in sample_seqs_idx(wl, 10):
-        for i in range(4):
+        for i in range(nqv):
             row = starts[s] + i
-            cut = np.array([wl.seq_lens[s] - 4 + i + 1], np.int32)
+            cut = np.array([wl.seq_lens[s] - nqv + i + 1], np.int32)
             want = oracle.paged_decode_ref(qr[row:row + 1], kc, vc, wl.block_tables[s:s + 1], cut, wl.scale, "bf16")
             d = np.abs(g[row] - want[0])
             worst = max(worst, float(d.max()))
             assert np.all(d <= TOL["bf16"] + HALF_ULP["bf16"] * np.abs(want[0])), (s, i)
-    print(f"verify 8B batch: max-abs {worst:.3e} on sampled rows", flush=True)
+    print(f"verify 8B batch, {nqv} rows: max-abs {worst:.3e} on sampled rows", flush=True)
 
 
 def sample_seqs_idx(wl, n):
