@@ -207,6 +207,28 @@ def test_few_rows_many_segments_per_range(dtype, Hq, Hkv, max_q):
     assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 8), ("f16", 64, 8, 4), ("bf16", 32, 8, 4)])
+def test_few_rows_many_segments_fp8_pools(dtype, Hq, Hkv, max_q):
+    """The few-row split over fp8 (e4m3) pools, one and two tile waves per kv
+    head, over hundreds of short sequences; every row against the oracle."""
+    rng = np.random.default_rng(Hq * 20 + Hkv + max_q)
+    S = 400
+    lens = rng.integers(1, 200, size=S)
+    lens[::23] = rng.integers(400, 900, size=len(lens[::23]))
+    nq = np.minimum(rng.integers(0, max_q + 1, size=S), lens)
+    wl, starts, q = _case(800 + Hq + max_q, Hq, Hkv, 128, dtype, lens, nq)
+    kc8, vc8 = W.with_fp8_pools(wl, 83)
+    ks, vs = 1.0 / 128, 1.0 / 96
+    g = _gpu(wl, starts, q, kc8, vc8, fp8=(ks, vs), max_q=max_q)
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), kc8.numpy(), vc8.numpy(), wl.block_tables, wl.seq_lens, starts,
+                                   wl.scale, dtype, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    diff = np.abs(g - ref)
+    print(f"{S} short sequences over fp8 pools {dtype} {Hq}/{Hkv} up to {max_q} rows: max-abs {diff.max():.3e}",
+          flush=True)
+    assert np.isfinite(g).all()
+    assert float(np.max(diff - (TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)))) <= 0.0
+
+
 @pytest.mark.parametrize("nqv", [4, 8])
 def test_verify_8b_batch_full_size(nqv):
     """Speculative verification on the 8B-shaped batch (4 or 8 query rows per
