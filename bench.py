@@ -6,19 +6,28 @@ split path: the partition kernel plus the log-sum-exp reduce), with the
 inputs already resident in HBM.  Prints ONE JSON line:
 
   value        KV GB/s = (bytes of K and V of the valid tokens) / (wall time per step)
-  ms_per_step  wall time per step between two device synchronisations
-  roofline     the decode launch: algorithmic KV bytes / its mean duration from
-               HIP events on the launch stream, against 8000 GB/s HBM3E peak
-  cpu_baseline the float64 oracle, single thread, on a bounded sample of the
-               same workload (first sequences, ~10 s of CPU work)
+  ms_per_step  wall time per step: K steps back to back between two device
+               synchronisations
+  us_per_step_flushed
+               the same step timed alone, N times: before each, an untimed
+               512 MiB write evicts the caches (L2 and MALL), then one pair of
+               HIP events on the launch stream brackets the step; p10/p50/p90
+  roofline     the decode launches: algorithmic KV bytes / their mean duration
+               (one pair of HIP events around the K back-to-back steps on the
+               launch stream), against 8000 GB/s HBM3E peak; the flushed
+               median gives ``frac_flushed_p50``
+  cpu_baseline the float64 oracle on the host cores: a process pool over the
+               batch's sequences (one BLAS thread per process), run before the
+               GPU is touched; a one-core walk of the same batch beside it
 
 Workload (default): 8B-shaped GQA decode batch, 256 sequences, 32 query / 8
 kv heads, head_size 128, bf16, block_size 16, lognormal lengths (median 1024,
 sigma 1, clipped to [16, 4096]), shuffled block pool.  Synthetic N(0, 1) data.
 
 Other lines (``--op``): ``copy_blocks`` times the copy-on-write block copies on
-the same pool layout (HBM roofline); ``block_manager`` times the host block
-manager building one decode step of a 256-sequence batch.
+the same pool layout (HBM roofline); ``prefill`` the multi-token rows
+(speculative verification or a chunked prefill); ``block_manager`` times the
+host block manager building one decode step of a 256-sequence batch.
 """
 
 from __future__ import annotations
@@ -59,7 +68,12 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--partition", type=int, default=-1, help="tokens per partition; -1 = workload default")
     ap.add_argument("--flags", type=int, default=-1, help="decode flags (1 = shared blocks); -1 = workload default")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of each oracle leg (the process pool and the one-core walk)")
+    ap.add_argument("--cpu-cores", type=int, default=0,
+                    help="oracle processes; 0 = the cores this process may run on, at most 16")
+    ap.add_argument("--flush-iters", type=int, default=100,
+                    help="steps timed one by one after a 512 MiB cache-evicting write (p10/p50/p90)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="capture the decode step in a HIP graph and time replays")
     ap.add_argument("--graph-calls", type=int, default=1, metavar="N",
@@ -167,10 +181,46 @@ def write_traffic(args):
     print(json.dumps({key: db[key]}))
 
 
-def cpu_baseline(wl, seconds: float, gpu_out, fp8_pools=None):
-    """Time the oracle (single thread) on the workload's sequences in order
-    (over the fp8 code pools when given) until ``seconds`` of oracle time are
-    spent; a batch that takes less is walked again from its first sequence."""
+FLUSH_BYTES = 512 << 20
+_ORACLE = {}                                     # inputs the oracle processes inherit (fork, no GPU yet)
+
+
+def host_cores(requested: int = 0) -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    n = min(n, 16)
+    return max(1, min(requested, n) if requested > 0 else n)
+
+
+def _oracle_init():
+    from threadpoolctl import threadpool_limits
+    _ORACLE["limits"] = threadpool_limits(1)      # one BLAS thread per process
+
+
+def _oracle_seq(s: int):
+    import oracle
+    st = _ORACLE
+    t0 = time.perf_counter()
+    ref = oracle.paged_decode_ref(st["q"], st["kc"], st["vc"], st["bt"], st["sl"], st["scale"], st["dtype"],
+                                  seqs=[s], **st["extra"])
+    return s, ref[0], time.perf_counter() - t0
+
+
+def cpu_baseline(wl, seconds: float, cores: int, fp8_pools=None):
+    """The float64 oracle over the workload's sequences, on the host cores.
+
+    Must run before this process touches the GPU: the pool forks it.
+    * pool leg: ``cores`` processes (one BLAS thread each) walk the batch's
+      sequences, whole passes, until ``seconds`` of wall time are spent;
+    * one-core leg: the same walk in this process, one thread, for
+      ``seconds``;
+    * the tiny MHA batch (4 sequences, fp32) once on one core.
+    Returns (record, {sequence: oracle output}) for the sequences walked.
+    """
+    import multiprocessing as mp
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -182,31 +232,101 @@ def cpu_baseline(wl, seconds: float, gpu_out, fp8_pools=None):
     if fp8_pools is not None:
         kc, vc = fp8_pools[0].numpy(), fp8_pools[1].numpy()
         extra = dict(kv_dtype="e4m3", k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    if wl.slot_mapping is not None:                 # the new tokens' rows, as the GPU step scatters them
+        nk, nv = W.raw_numpy(wl.new_key), W.raw_numpy(wl.new_value)
+        if fp8_pools is not None:
+            kc, vc = oracle.reshape_and_cache_fp8_ref(nk, nv, kc, vc, wl.slot_mapping, wl.dtype, FP8_K_SCALE,
+                                                      FP8_V_SCALE)
+        else:
+            kc, vc = oracle.reshape_and_cache_ref(nk, nv, kc, vc, wl.slot_mapping)
+    _ORACLE.update(q=q, kc=kc, vc=vc, bt=wl.block_tables, sl=wl.seq_lens, scale=wl.scale, dtype=wl.dtype,
+                   extra=extra)
     S = wl.num_seqs
-    done, tok, elapsed, err = 0, 0, 0.0, 0.0
+    e = 1 if fp8_pools is not None else W.ELEM_BYTES[wl.dtype]
+    seq_bytes = wl.seq_lens.astype(np.int64) * wl.num_kv_heads * wl.head_size * 2 * e
+    refs = {}
+
+    # pool leg: whole passes over the batch (sequences longest first, so the pass ends evenly)
+    order = [int(s) for s in np.argsort(-wl.seq_lens, kind="stable")]
+    passes, t0 = 0, time.perf_counter()
+    with mp.get_context("fork").Pool(cores, initializer=_oracle_init) as pool:
+        while passes == 0 or (time.perf_counter() - t0 < seconds and passes < 64):
+            for s, ref, _ in pool.imap_unordered(_oracle_seq, order, chunksize=1):
+                refs.setdefault(s, ref)
+            passes += 1
+    pool_s = time.perf_counter() - t0
+    pool_bytes = passes * int(seq_bytes.sum())
+
+    # one-core leg: sequences in order, in this process
+    done, el = 0, 0.0
     with threadpool_limits(1):
-        while elapsed < seconds and done < 64 * S:
-            s = done % S
-            t0 = time.perf_counter()
-            ref = oracle.paged_decode_ref(q, kc, vc, wl.block_tables, wl.seq_lens, wl.scale, wl.dtype,
-                                          seqs=[s], **extra)
-            elapsed += time.perf_counter() - t0
-            if done < S:
-                g = gpu_out[s].double().numpy()
-                err = max(err, float(np.max(np.abs(g - ref[0]))))
-            tok += int(wl.seq_lens[s])
+        while el < seconds and done < 64 * S:
+            _, _, dt = _oracle_seq(done % S)
+            el += dt
             done += 1
-    kv = tok * wl.num_kv_heads * wl.head_size * 2 * (1 if fp8_pools is not None else W.ELEM_BYTES[wl.dtype])
-    walked = (f"first {done} of {S} sequences" if done <= S else
-              f"{done // S} passes over all {S} sequences" + (f" and the first {done % S} again" if done % S else ""))
-    return {
-        "value": round(kv / elapsed / 1e9, 4),
+    one_bytes = int(sum(int(seq_bytes[i % S]) for i in range(done)))
+
+    # the tiny MHA batch, whole, on one core
+    tiny = W.make_config(1, 0, poison=False)
+    with threadpool_limits(1):
+        t1 = time.perf_counter()
+        oracle.paged_decode_ref(W.raw_numpy(tiny.query), W.raw_numpy(tiny.k_cache), W.raw_numpy(tiny.v_cache),
+                                tiny.block_tables, tiny.seq_lens, tiny.scale, tiny.dtype)
+        tiny_s = time.perf_counter() - t1
+    rec = {
+        "value": round(pool_bytes / pool_s / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{walked} ({tok} tokens, {kv} KV bytes) of the same workload, float64 NumPy, "
-                  f"one thread, {elapsed:.2f} s",
-    }, err
+        "sample": f"{passes} whole passes over all {S} sequences of the same workload ({pool_bytes} KV bytes), "
+                  f"float64 NumPy, {cores} processes x 1 BLAS thread, {pool_s:.2f} s wall",
+        "one_core": {"value": round(one_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                     "sample": f"{done} sequences walked in order ({one_bytes} KV bytes), one thread, {el:.2f} s"},
+        "tiny_mha_one_core_us": round(tiny_s * 1e6, 1),
+    }
+    return rec, refs
+
+
+def timed_steps(step, stream, K: int, warmup: int, flush_iters: int, device):
+    """W untimed steps; K steps back to back between two synchronisations
+    (wall clock, and one pair of HIP events on ``stream`` for the mean launch
+    time); then ``flush_iters`` steps each after an untimed 512 MiB write,
+    each bracketed by its own pair of events on ``stream``."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(K):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_ms = ev0.elapsed_time(ev1) / K
+    flushed = []
+    if flush_iters > 0:
+        scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(flush_iters)]
+        with torch.cuda.stream(stream):
+            for i, (a, b) in enumerate(evs):
+                scratch.fill_(i & 255)
+                a.record(stream)
+                step()
+                b.record(stream)
+        torch.cuda.synchronize()
+        flushed = [a.elapsed_time(b) for a, b in evs]
+        del scratch
+    dist = None
+    if flushed:
+        p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(flushed, [10, 50, 90]))
+        dist = {"p10": round(p10, 2), "p50": round(p50, 2), "p90": round(p90, 2), "n": len(flushed),
+                "flush_bytes": FLUSH_BYTES}
+    return wall, mean_ms, dist
 
 
 COPY_PAIRS, COPY_POOL = 4096, 25000
@@ -313,19 +433,10 @@ def bench_prefill(args):
     def step():
         P.paged_attention_prefill(out, q, kc, vc, bt, sl, qs, wl.scale, max_query_len=mq, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     K = args.steps
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(K):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / K
-    launch = ev0.elapsed_time(ev1) / K / 1e3
+    wall, mean_ms, dist = timed_steps(step, stream, K, args.warmup, args.flush_iters, dev)
+    wall /= K
+    launch = mean_ms / 1e3
     D, Hq = wl.head_size, wl.num_heads
     # (query row, visible key) pairs: row i of n sees L - n + i + 1 keys
     pairs = int(sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2 for n, L in zip(nq, wl.seq_lens)))
@@ -338,6 +449,7 @@ def bench_prefill(args):
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": desc, "query_tokens": T, "kv_bytes": kv, "flops": flops},
+        "us_per_step": round(wall * 1e6, 2), "us_per_step_flushed": dist, "launch_us": round(launch * 1e6, 2),
         "roofline": ({"bound": "hbm", "achieved": round(kv / launch / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(kv / launch / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                       "kernel": ("pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel"
@@ -458,15 +570,16 @@ def main():
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     sys.path.insert(0, ROOT)
     import paged_kv_cache_291_amd as P
-    from paged_kv_cache_291_amd import workloads as W
 
     if args.op == "block_manager":
         print(json.dumps(bench_block_manager(args)))
+        return
+    if args.op == "decode":
+        print(json.dumps(bench_decode(args)), flush=True)
         return
     if not torch.cuda.is_available():
         print("no HIP device visible", file=sys.stderr)
@@ -478,26 +591,53 @@ def main():
     if args.op == "prefill":
         print(json.dumps(bench_prefill(args)))
         return
+
+
+WORKLOADS = {1: "tiny MHA paged decode (4 seqs, 8/8 heads, D=64, fp32)",
+             2: "13B-shaped MHA paged decode (64 seqs, 40/40 heads, D=128, fp16)",
+             3: "8B-shaped GQA paged decode (256 seqs, 32/8 heads, D=128, bf16)",
+             4: "long-context GQA paged decode (8 seqs x 32768, 64/8 heads, D=128, bf16)",
+             5: "shared-prefix GQA paged decode (128 seqs, 1024-token shared prefix, 32/8 heads, bf16)"}
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_291_amd as P
+    from paged_kv_cache_291_amd import workloads as W
+
     cfg = args.config
     ps = DEFAULT_PARTITION[cfg] if args.partition < 0 else args.partition
     flags = DEFAULT_FLAGS.get(cfg, 0) if args.flags < 0 else args.flags
-
+    fp8 = args.kv == "fp8"
     t0 = time.time()
     wl = W.make_config(cfg, args.seed, poison=False)
-    print(f"[bench] workload cfg{cfg} generated in {time.time() - t0:.1f}s: S={wl.num_seqs} "
-          f"tokens={int(wl.seq_lens.sum())} kv_bytes={wl.kv_bytes()}", file=sys.stderr, flush=True)
-    dev = torch.device("cuda:0")
-    q = wl.query.to(dev)
-    fp8 = args.kv == "fp8"
     if fp8 and wl.dtype == "f32":
         print("fp8 pools need a bf16 or fp16 query", file=sys.stderr)
         sys.exit(2)
+    print(f"[bench] workload cfg{cfg} generated in {time.time() - t0:.1f}s: S={wl.num_seqs} "
+          f"tokens={int(wl.seq_lens.sum())} kv_bytes={wl.kv_bytes()}", file=sys.stderr, flush=True)
+    kc_host, vc_host = wl.k_cache, wl.v_cache
     if fp8:
         kc_host = W.random_fp8_codes(1000 + args.seed, tuple(wl.k_cache.shape))
         vc_host = W.random_fp8_codes(1001 + args.seed, tuple(wl.v_cache.shape))
-        kc, vc = kc_host.to(dev), vc_host.to(dev)
-    else:
-        kc, vc = wl.k_cache.to(dev), wl.v_cache.to(dev)
+
+    # the oracle legs run first: the pool forks this process, which must not have touched the GPU yet
+    cb, refs = None, {}
+    if not args.no_cpu_baseline:
+        cores = host_cores(args.cpu_cores)
+        print(f"[bench] oracle on {cores} host cores ({args.cpu_seconds:.0f} s per leg)", file=sys.stderr,
+              flush=True)
+        cb, refs = cpu_baseline(wl, args.cpu_seconds, cores, (kc_host, vc_host) if fp8 else None)
+
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    P.load_library()
+    dev = torch.device("cuda:0")
+    q = wl.query.to(dev)
+    kc, vc = kc_host.to(dev), vc_host.to(dev)
     bt = torch.from_numpy(wl.block_tables).to(dev)
     sl = torch.from_numpy(wl.seq_lens).to(dev)
     out = torch.empty_like(q)
@@ -505,10 +645,15 @@ def main():
     need = P.decode_workspace_bytes(q, bt, wl.block_size, ps, wl.max_seq_len)
     if need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    if wl.slot_mapping is not None:
-        scatter = (lambda *a: P.reshape_and_cache_fp8(*a, FP8_K_SCALE, FP8_V_SCALE)) if fp8 else P.reshape_and_cache
-        scatter(wl.new_key.to(dev), wl.new_value.to(dev), kc, vc, torch.from_numpy(wl.slot_mapping).to(dev))
     stream = torch.cuda.current_stream()
+    scatter_us = None
+    if wl.slot_mapping is not None:
+        nk, nv = wl.new_key.to(dev), wl.new_value.to(dev)
+        sm = torch.from_numpy(wl.slot_mapping).to(dev)
+        scatter = (lambda: P.reshape_and_cache_fp8(nk, nv, kc, vc, sm, FP8_K_SCALE, FP8_V_SCALE, stream=stream)
+                   ) if fp8 else (lambda: P.reshape_and_cache(nk, nv, kc, vc, sm, stream=stream))
+        _, sc_ms, _ = timed_steps(scatter, stream, 100, 10, 0, dev)   # idempotent: the same rows each time
+        scatter_us = round(sc_ms * 1e3, 2)
 
     def decode(stream_):
         if fp8:
@@ -519,57 +664,44 @@ def main():
             P.paged_attention_decode(out, q, kc, vc, bt, sl, wl.scale, partition_size=ps,
                                      max_seq_len=wl.max_seq_len, workspace=ws, flags=flags, stream=stream_)
 
-    def step():
-        decode(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    step = lambda: decode(stream)                      # noqa: E731
+    calls = 1
     if args.graph:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):                  # launches go to the capturing stream
             for _ in range(args.graph_calls):
                 decode(None)
         stream = torch.cuda.current_stream()
         step = graph.replay
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
+        calls = args.graph_calls                       # decode calls per timed replay
     K = args.steps
-    # Two HIP events on the launch stream bracket the K calls: an event between
-    # calls would put its own marker packet (and a gap) between the kernels.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(K):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    launch_ms = np.array([ev0.elapsed_time(ev1) / K])
-
-    calls = args.graph_calls if args.graph else 1      # decode calls per timed replay
+    wall, mean_ms, dist = timed_steps(step, stream, K, args.warmup, args.flush_iters, dev)
     wall /= calls
-    launch_ms = launch_ms / calls
-    kv = wl.kv_bytes() // W.ELEM_BYTES[wl.dtype] if fp8 else wl.kv_bytes()
+    mean_ms /= calls
+    if dist is not None and calls > 1:
+        dist = {k: (round(v / calls, 2) if k.startswith("p") else v) for k, v in dist.items()}
+
+    e = 1 if fp8 else W.ELEM_BYTES[wl.dtype]
+    kv = wl.kv_bytes() // W.ELEM_BYTES[wl.dtype] * e
+    kv_unique = wl.kv_bytes_unique() // W.ELEM_BYTES[wl.dtype] * e
+    shared = kv_unique < kv                            # blocks named by several sequences
+    roof_bytes = kv_unique if shared else kv
     ms_per_step = wall * 1e3 / K
     value = kv / (wall / K) / 1e9
-    mean_launch_s = float(launch_ms.mean()) / 1e3
-    achieved = kv / mean_launch_s / 1e9
-    workload = {1: "tiny MHA paged decode (4 seqs, 8/8 heads, D=64, fp32)",
-                2: "13B-shaped MHA paged decode (64 seqs, 40/40 heads, D=128, fp16)",
-                3: "8B-shaped GQA paged decode (256 seqs, 32/8 heads, D=128, bf16)",
-                4: "long-context GQA paged decode (8 seqs x 32768, 64/8 heads, D=128, bf16)",
-                5: "shared-prefix GQA paged decode (128 seqs, 1024-token shared prefix, 32/8 heads, bf16)"}[cfg]
+    achieved = roof_bytes / (mean_ms / 1e3) / 1e9
     if wl.dtype == "f32":
         kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 else "")
     else:
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
         if fp8:
             kernel += "|fp8"
-    # the decode kernel moves almost all bytes; the key lists the step's kernels by traffic
-    out_host = out.cpu()
+    out_host = out.cpu().double().numpy()
+    err = None
+    if refs:
+        err = max(float(np.max(np.abs(out_host[s] - r))) for s, r in refs.items())
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -584,7 +716,7 @@ def main():
         "dtype": wl.dtype + ("/e4m3 KV" if fp8 else ""),
         "data": "synthetic",
         "config": {
-            "workload": workload + (", over e4m3 (fp8) K/V pools" if fp8 else ""),
+            "workload": WORKLOADS[cfg] + (", over e4m3 (fp8) K/V pools" if fp8 else ""),
             "num_seqs": wl.num_seqs, "num_heads": wl.num_heads, "num_kv_heads": wl.num_kv_heads,
             "head_size": wl.head_size, "block_size": wl.block_size, "num_blocks": wl.num_blocks,
             "total_tokens": int(wl.seq_lens.sum()), "max_seq_len": wl.max_seq_len,
@@ -592,25 +724,28 @@ def main():
             "launch": f"HIP graph replay, {args.graph_calls} calls per graph" if args.graph else "eager",
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_flushed": dist,
         "kv_bytes_per_step": kv,
+        "kv_bytes_unique": kv_unique,
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "launch_us": round(float(launch_ms.mean()) * 1e3, 2),
+        "launch_us": round(mean_ms * 1e3, 2),
+        "scatter_us": scatter_us,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac_flushed_p50": (round(roof_bytes / (dist["p50"] / 1e6) / 1e9 / HBM_PEAK_GBS, 4)
+                                 if dist else None),
             "traffic": traffic_for(kernel, f"cfg{cfg}"),
             "kernel": kernel,
-            "bytes_per_launch": kv,
+            "bytes_per_launch": roof_bytes,
+            "bytes": "unique K/V rows (a shared block counts once)" if shared else "K/V rows of the valid tokens",
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cb,
+        "max_abs_err_vs_oracle": err,
     }
-    if not args.no_cpu_baseline:
-        cb, err = cpu_baseline(wl, args.cpu_seconds, out_host, (kc_host, vc_host) if fp8 else None)
-        rec["cpu_baseline"] = cb
-        rec["max_abs_err_vs_oracle_on_cpu_sample"] = err
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -619,7 +754,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         rec["copy_calibration_bytes"] = n
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 if __name__ == "__main__":

@@ -81,6 +81,15 @@ class Workload:
         e = ELEM_BYTES[self.dtype]
         return int(self.seq_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_size * 2 * e
 
+    def kv_bytes_unique(self) -> int:
+        """Bytes of the distinct K/V rows the step reads: a slot named by
+        several sequences (a shared prefix) counts once."""
+        e = ELEM_BYTES[self.dtype]
+        slots = [_slots_of(self.block_tables, s, np.arange(int(L)), self.block_size)
+                 for s, L in enumerate(self.seq_lens.tolist()) if L > 0]
+        n = len(np.unique(np.concatenate(slots))) if slots else 0
+        return n * self.num_kv_heads * self.head_size * 2 * e
+
 
 def raw_numpy(t: torch.Tensor) -> np.ndarray:
     """Stored elements of a CPU tensor as numpy: float32, float16, or the

@@ -1,11 +1,10 @@
 """GPU parity of paged_attention_decode against the float64 oracle.
 
 Runs through the C ABI (ctypes binding).  The five workloads are run at their
-full sizes in the launch configuration the benchmark times, compared with the
-oracle on sampled sequences (shortest, longest and a seeded sample), and
-checked for finiteness everywhere (the pool holds NaN outside the rows the
-tables name, so any masking mistake shows).  Small random shapes are compared
-element by element on every output.
+full sizes in the launch configuration the benchmark times and compared with
+the oracle on every sequence, head and element (the pool holds NaN outside
+the rows the tables name, so any masking mistake shows).  Small random shapes
+are compared element by element on every output.
 """
 
 import zlib
@@ -17,7 +16,7 @@ import torch
 import paged_kv_cache_291_amd as P
 from paged_kv_cache_291_amd import workloads as W
 
-from helpers import HALF_ULP, TOL, errors, gpu_decode, oracle_decode, sample_seqs, to_device
+from helpers import TOL, assert_parity, errors, gpu_decode, oracle_decode, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -25,16 +24,14 @@ pytestmark = pytest.mark.gpu
 CONFIG_PARTITIONS = {1: (0, 16), 2: (0, 512), 3: (0, 512), 4: (0, 512), 5: (0, 512)}
 # workloads whose blocks are shared between sequences also run with the cacheable-load flag
 CONFIG_FLAGS = {5: P.PA_FLAG_SHARED_BLOCKS}
-SAMPLE = {1: 4, 2: 6, 3: 12, 4: 8, 5: 8}
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_config_parity(cfg, seed):
     wl = W.make_config(cfg, seed, poison=True)
-    seqs = sample_seqs(wl, SAMPLE[cfg], seed)
-    print(f"cfg{cfg} seed{seed}: S={wl.num_seqs} tokens={int(wl.seq_lens.sum())} sample={seqs}", flush=True)
-    ref = oracle_decode(wl, seqs)
+    print(f"cfg{cfg} seed{seed}: S={wl.num_seqs} tokens={int(wl.seq_lens.sum())}", flush=True)
+    ref = oracle_decode(wl)
     dev = to_device(wl)
     if wl.slot_mapping is not None:
         P.reshape_and_cache(dev["nk"], dev["nv"], dev["kc"], dev["vc"], dev["sm"])
@@ -44,9 +41,9 @@ def test_config_parity(cfg, seed):
         runs += [(ps, CONFIG_FLAGS[cfg]) for ps in CONFIG_PARTITIONS[cfg]]
     for ps, flags in runs:
         out, _ = gpu_decode(wl, dev, partition_size=ps, scatter=False, flags=flags)
-        assert torch.isfinite(out.float()).all(), f"non-finite output (partition {ps}, flags {flags})"
-        err, _, _ = errors(out[seqs], ref)
+        err, _, _ = errors(out, ref)
         print(f"  partition={ps} flags={flags}: max-abs err {err:.3e} (tol {TOL[wl.dtype]})", flush=True)
+        assert torch.isfinite(out.float()).all(), f"non-finite output (partition {ps}, flags {flags})"
         assert err <= TOL[wl.dtype]
         if flags:
             assert torch.equal(out, outs[(ps, 0)])          # the cache policy changes no arithmetic
@@ -72,12 +69,8 @@ def test_sweep_all_outputs(dtype, D, Hq, Hkv, ps):
     wl = W.make_random(seed, len(EDGE_LENS), Hq, Hkv, D, dtype, EDGE_LENS, extra_table_cols=2)
     out, _ = gpu_decode(wl, partition_size=ps)
     ref = oracle_decode(wl)
-    _, g, diff = errors(out, ref)
-    bound = TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)
-    worst = float(np.max(diff - bound))
-    print(f"{dtype} D={D} {Hq}/{Hkv} ps={ps}: max-abs {diff.max():.3e}", flush=True)
-    assert np.isfinite(g).all()
-    assert worst <= 0.0
+    _, g, _ = errors(out, ref)
+    assert_parity(g, ref, dtype, f"{dtype} D={D} {Hq}/{Hkv} ps={ps}")
     assert (g[0] == 0).all()                           # empty sequence
     # one token: softmax weight is exactly 1, the output is that token's value
     one = EDGE_LENS.index(1)
@@ -133,10 +126,8 @@ def test_many_short_sequences(dtype, Hq, Hkv):
     ref = oracle_decode(wl)
     for ps, flags in ((0, 0), (0, P.PA_FLAG_SHARED_BLOCKS), (32, 0)):
         out, _ = gpu_decode(wl, partition_size=ps, flags=flags)
-        _, g, diff = errors(out, ref)
-        bound = TOL[dtype] + HALF_ULP[dtype] * np.abs(ref)
-        assert np.isfinite(g).all()
-        assert float(np.max(diff - bound)) <= 0.0, (ps, flags, float(diff.max()))
+        _, g, _ = errors(out, ref)
+        assert_parity(g, ref, dtype, f"700 short sequences {dtype} {Hq}/{Hkv} ps={ps} flags={flags}")
         assert (g[lens == 0] == 0).all()
 
 
@@ -156,10 +147,8 @@ def test_fixed_split_item_pairing(S, Hq, Hkv, max_len):
     assert wl.max_seq_len == max_len
     ref = oracle_decode(wl)
     out, _ = gpu_decode(wl, partition_size=512)
-    _, g, diff = errors(out, ref)
-    bound = TOL["f16"] + HALF_ULP["f16"] * np.abs(ref)
-    assert np.isfinite(g).all()
-    assert float(np.max(diff - bound)) <= 0.0, float(diff.max())
+    _, g, _ = errors(out, ref)
+    assert_parity(g, ref, "f16", f"fixed split S={S} {Hq}/{Hkv} max_len={max_len}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -184,7 +173,7 @@ def test_contract_violations_give_nan_rows(dtype, ps):
     for s in bad:
         assert np.isnan(g[s]).all(), s
     ref = oracle_decode(wl, seqs=good)
-    assert np.max(np.abs(g[good] - ref)) <= TOL[dtype] + HALF_ULP[dtype] * np.max(np.abs(ref))
+    assert_parity(g[good], ref, dtype, "rows beside the out-of-contract ones")
 
 
 def _decode_with(wl, ws, ps=0):
@@ -208,9 +197,7 @@ def test_workspace_reuse_and_empty_batches():
     wb = W.make_random(502, len(lens_b), 32, 8, 128, "bf16", lens_b)
     for wl in (wa, wb, wa):
         g = _decode_with(wl, ws)
-        ref = oracle_decode(wl)
-        assert np.isfinite(g).all()
-        assert float(np.max(np.abs(g - ref) - (TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref)))) <= 0.0
+        assert_parity(g, oracle_decode(wl), "bf16", f"workspace reuse, {wl.num_seqs} sequences")
     empty = W.make_random(503, 5, 32, 8, 128, "bf16", [0, 0, 0, 0, 0])
     assert (_decode_with(empty, ws) == 0).all()
     sl = empty.seq_lens.copy()
@@ -224,7 +211,7 @@ def test_workspace_reuse_and_empty_batches():
 def test_largest_batch_balanced_split():
     """16383 sequences, the most the balanced split takes (its prefix sums
     fill 64 KiB of LDS; the multi-token variant stages twice that): decode and
-    one-row multi-token calls against the oracle on sampled sequences."""
+    one-row multi-token calls against the oracle on every sequence."""
     S = 16383
     lens = (np.arange(S) % 5).astype(np.int32) + 1
     wl = W.make_random(9, S, 8, 2, 64, "bf16", lens)
@@ -235,9 +222,6 @@ def test_largest_batch_balanced_split():
     P.paged_attention_prefill(out2, d["q"], d["kc"], d["vc"], d["bt"], d["sl"],
                               torch.arange(0, S + 1, dtype=torch.int32, device="cuda"), wl.scale, max_query_len=1)
     torch.cuda.synchronize()
-    seqs = [0, 1, 7, 4097, 8000, S - 2, S - 1]
-    ref = oracle_decode(wl, seqs=seqs)
-    for o in (out, out2):
-        g = o.cpu().double().numpy()[seqs]
-        assert np.all(np.abs(g - ref) <= TOL["bf16"] + HALF_ULP["bf16"] * np.abs(ref))
-    assert torch.isfinite(out.float()).all() and torch.isfinite(out2.float()).all()
+    ref = oracle_decode(wl)
+    for o, what in ((out, "decode"), (out2, "one-row multi-token")):
+        assert_parity(o.cpu().double().numpy(), ref, "bf16", f"16383 sequences, {what}")

@@ -1,7 +1,10 @@
 """A decode step (and a whole serving step: copies, scatter, decode) captured
 in a HIP graph replays to the same bytes as eager calls, and reads its inputs
 live: inputs changed in place between replays change the output exactly as
-they would eagerly.  Eager work and synchronisations run between replays."""
+they would eagerly.  Eager work and synchronisations run between replays.
+Every replay's output is also compared with the float64 oracle over the
+inputs of that replay (devpress.csdn.net vLLM architecture article, section
+1: the worker captures the step in a graph to cut launch overhead)."""
 
 from __future__ import annotations
 
@@ -9,9 +12,12 @@ import numpy as np
 import pytest
 import torch
 
+from dataclasses import replace
+
+import oracle
 import paged_kv_cache_291_amd as P
 from paged_kv_cache_291_amd import workloads as W
-from helpers import to_device
+from helpers import assert_parity, oracle_decode, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +60,8 @@ def test_decode_graph_replays_match_eager(cfg, ps):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), i
-        assert torch.isfinite(out.float()).all()
+        ref = oracle_decode(replace(wl, query=qi.cpu()))
+        assert_parity(out.cpu().double().numpy(), ref, wl.dtype, f"cfg{cfg} ps={ps} replay {i} vs oracle")
 
 
 def test_serving_step_graph():
@@ -128,4 +135,8 @@ def test_serving_step_graph():
         print(f"serving replay {i}: {copies} copies so far", flush=True)
         assert torch.equal(out, eager) or i == 0
         assert torch.equal(kc, kc_e) and torch.equal(vc, vc_e)
+        if i > 0:                                              # a replay: the pools hold what it scattered
+            ref = oracle.paged_decode_ref(W.raw_numpy(q.cpu()), W.raw_numpy(kc.cpu()), W.raw_numpy(vc.cpu()),
+                                          bt_d.cpu().numpy(), sl_d.cpu().numpy(), D ** -0.5, "bf16")
+            assert_parity(out.cpu().double().numpy(), ref, "bf16", f"serving replay {i} vs oracle")
     assert copies > 0

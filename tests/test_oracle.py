@@ -127,18 +127,16 @@ def _as_pyfloat(x, dtype):
     return float(x)
 
 
-def brute_force(q, kc, vc, tables, lens, scale, dtype):
+def _rows_via_inverse(kc, vc, tables, lens, dtype):
     """Pure Python: walk the pool block by block through the inverse of the
-    block tables, collect each sequence's rows, then softmax attention with
-    math.exp and math.fsum."""
-    S, Hq, D = len(q), len(q[0]), len(q[0][0])
+    block tables and collect each sequence's rows: (s, t, kvh) -> (k, v)."""
+    S = len(lens)
     NB, BS, Hkv = len(kc), len(kc[0]), len(kc[0][0])
-    G = Hq // Hkv
     users = defaultdict(list)                      # physical block -> [(seq, logical block)]
     for s in range(S):
         for j in range((int(lens[s]) + BS - 1) // BS):
             users[int(tables[s][j])].append((s, j))
-    rows = {}                                      # (s, t, kvh) -> (k row, v row)
+    rows = {}
     for b in range(NB):
         for (s, j) in users.get(b, []):
             for off in range(BS):
@@ -147,6 +145,26 @@ def brute_force(q, kc, vc, tables, lens, scale, dtype):
                     for kvh in range(Hkv):
                         rows[(s, t, kvh)] = ([_as_pyfloat(x, dtype) for x in kc[b][off][kvh]],
                                              [_as_pyfloat(x, dtype) for x in vc[b][off][kvh]])
+    return rows
+
+
+def _weights(qh, rows, s, L, kvh, scale):
+    """Softmax weights of one query over the rows, with math.exp and math.fsum."""
+    D = len(qh)
+    z = [scale * math.fsum(qh[d] * rows[(s, t, kvh)][0][d] for d in range(D)) for t in range(L)]
+    m = max(z)
+    e = [math.exp(zt - m) for zt in z]
+    den = math.fsum(e)
+    return [x / den for x in e], e, den
+
+
+def brute_force(q, kc, vc, tables, lens, scale, dtype):
+    """Pure Python: rows collected through the inverse table, then softmax
+    attention with math.exp and math.fsum."""
+    S, Hq, D = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(kc[0][0])
+    G = Hq // Hkv
+    rows = _rows_via_inverse(kc, vc, tables, lens, dtype)
     out = [[[0.0] * D for _ in range(Hq)] for _ in range(S)]
     for s in range(S):
         L = int(lens[s])
@@ -154,11 +172,7 @@ def brute_force(q, kc, vc, tables, lens, scale, dtype):
             if L == 0:
                 continue
             kvh = h // G
-            qh = [_as_pyfloat(x, dtype) for x in q[s][h]]
-            z = [scale * math.fsum(qh[d] * rows[(s, t, kvh)][0][d] for d in range(D)) for t in range(L)]
-            m = max(z)
-            e = [math.exp(zt - m) for zt in z]
-            den = math.fsum(e)
+            _, e, den = _weights([_as_pyfloat(x, dtype) for x in q[s][h]], rows, s, L, kvh, scale)
             for d in range(D):
                 out[s][h][d] = math.fsum(e[t] * rows[(s, t, kvh)][1][d] for t in range(L)) / den
     return out
@@ -246,6 +260,39 @@ def test_unreferenced_blocks_never_read():
 
 
 # ---------------------------------------------------------------- P5: softmax rows
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2)])
+def test_softmax_rows_equal_brute_force_weights(dtype, Hq, Hkv):
+    """Every weight of every (sequence, head) row equals the pure-Python
+    weight of the same key, found through the inverse table: a wrong head,
+    a wrong gather or a dropped scale in the weights fails here."""
+    q, kc, vc, bt, sl = _tiny(dtype, Hq, Hkv, 2, (1, 5, 17), seed=40 + Hq)
+    rows = _rows_via_inverse(kc.tolist(), vc.tolist(), bt.tolist(), sl, dtype)
+    G = Hq // Hkv
+    for s in range(len(sl)):
+        for h in range(Hq):
+            p = oracle.paged_decode_probs_ref(q, kc, vc, bt, sl, 0.5, dtype, s, h)
+            want, _, _ = _weights([_as_pyfloat(x, dtype) for x in q[s][h].tolist()], rows, s, int(sl[s]),
+                                  h // G, 0.5)
+            assert np.max(np.abs(p - np.array(want))) <= 1e-14
+
+
+def test_softmax_rows_equal_dense_torch_softmax():
+    """The weights equal torch.softmax of the dense float64 scores of the
+    same query against its kv head's rows, taken by stacking whole blocks in
+    table order (a dense view of the sequence, not a per-token gather)."""
+    S, Hq, Hkv, D, L = 2, 8, 2, 32, 40
+    wl = W.make_random(13, S, Hq, Hkv, D, "f32", [L] * S, pool_factor=1.0)
+    q, kc, vc, bt, sl = raw(wl)
+    for s in range(S):
+        Kd = torch.from_numpy(kc[bt[s, :(L + 15) // 16]].reshape(-1, Hkv, D)[:L].astype(np.float64))
+        for h in range(Hq):
+            z = torch.from_numpy(q[s, h].astype(np.float64)) @ Kd[:, h // (Hq // Hkv)].T * wl.scale
+            want = torch.softmax(z, dim=0).numpy()
+            p = oracle.paged_decode_probs_ref(q, kc, vc, bt, sl, wl.scale, wl.dtype, s, h)
+            assert np.max(np.abs(p - want)) <= 1e-14
+
 
 def test_softmax_rows_sum_to_one():
     wl = W.make_random(6, 3, 8, 2, 32, "bf16", [1, 45, 300])
@@ -545,6 +592,41 @@ def test_e4m3_quantize_round_trip_and_ties():
             near_a, near_b = (lo, hi) if a < b else (hi, lo)
             assert int(oracle.quantize_e4m3_ref(np.array([near_a]), 1.0)[0]) == c | sgn
             assert int(oracle.quantize_e4m3_ref(np.array([near_b]), 1.0)[0]) == (c + 1) | sgn
+
+
+def test_e4m3_fp32_reciprocal_reading_is_within_one_code_of_exact_division():
+    """The quantisation reading multiplies by float32(1 / scale) in float32
+    (the decision is taken in the kernel's precision, the pages fixing
+    none).  Against exact division x / scale rounded to the nearest code
+    (ties to even) it differs by at most one code step, and only for values
+    within float32 rounding of a midpoint between two codes."""
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(4000) * rng.choice([0.01, 0.3, 3.0], size=4000)).astype(np.float32)
+    finite = np.array([c for c in range(256) if not np.isnan(oracle.E4M3_VALUES[c])])
+    vals = oracle.E4M3_VALUES[finite]
+    order = np.argsort(vals, kind="stable")
+    for scale in (1.0 / 96, 0.0123, 0.37):
+        got = oracle.quantize_e4m3_ref(x, scale)
+        y = np.clip(x.astype(np.float64) / scale, -448.0, 448.0)
+        near = []
+        for v in y.tolist():
+            d = np.abs(vals - v)
+            c = finite[d == d.min()]
+            if len(c) > 1:
+                c = [k for k in c if (k & 0x80) == (0x80 if np.signbit(v) else 0)] or list(c)
+                c = [k for k in c if k % 2 == 0] or list(c)
+            near.append(int(c[0]))
+        exact = np.array(near, dtype=np.uint8)
+        rank = np.empty(256, dtype=np.int64)
+        rank[finite[order]] = np.arange(len(finite))
+        steps = np.abs(rank[got] - rank[exact])
+        zero = (oracle.E4M3_VALUES[got] == 0) & (oracle.E4M3_VALUES[exact] == 0)
+        steps[zero] = 0                                   # +0 and -0
+        assert steps.max() <= 1, scale
+        for i in np.nonzero(steps)[0]:                    # only next to a midpoint
+            a, b = sorted((oracle.E4M3_VALUES[got[i]], oracle.E4M3_VALUES[exact[i]]))
+            mid = 0.5 * (a + b)
+            assert abs(y[i] - mid) <= 2.0 ** -22 * abs(mid), (scale, float(x[i]))
 
 
 def test_e4m3_quantize_saturation_nan_and_scale():
