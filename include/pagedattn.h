@@ -16,7 +16,9 @@
  * Conventions for the device entry points (the host block manager pa_bm_*
  * at the end has its own):
  *  - All data pointers are DEVICE pointers owned by the caller; the library
- *    never allocates or frees, keeps no global state, and is re-entrant.
+ *    never allocates or frees, keeps no global state, and is re-entrant
+ *    (paged_attention_decode_noalloc aside: it uses a device array of the
+ *    library's own, see there).
  *  - Tensors are dense and row-major in the shapes given; q, caches and
  *    outputs share one element type (enum pa_dtype) except where an entry
  *    point says otherwise (fp8 pools).  Data pointers must be 16-byte
@@ -48,7 +50,9 @@ typedef enum {
   PA_ERR_WORKSPACE = -3,    /* split path without a large enough workspace                   */
   PA_ERR_HIP = -4,          /* the HIP runtime reported an error at launch                   */
   PA_ERR_NO_BLOCKS = -5,    /* block manager: not enough free blocks in the pool             */
-  PA_ERR_CAPACITY = -6      /* block manager: the sequence's table would exceed its maximum  */
+  PA_ERR_CAPACITY = -6,     /* block manager: the sequence's table would exceed its maximum  */
+  PA_ERR_SCRATCH = -7       /* paged_attention_decode_noalloc: the call needs more scratch
+                               than PA_NOALLOC_SCRATCH_BYTES                                 */
 } pa_status;
 
 /* Element types.  PA_FP8_E4M3 (OCP 8-bit float, 1 sign, 4 exponent bits with
@@ -129,6 +133,39 @@ int paged_attention_decode(void* out, const void* query, const void* k_cache, co
                            int block_size, int max_blocks_per_seq, int num_blocks,
                            int max_seq_len, float scale, int dtype, int partition_size,
                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes exactly what
+ * paged_attention_decode computes (same kernels, bit-identical results) and
+ * takes the same arguments minus workspace and workspace_bytes.
+ *
+ * In place of the workspace it uses a device array of the library's own,
+ * PA_NOALLOC_SCRATCH_BYTES (32 MiB) per device, which each device the
+ * library runs on holds until the process ends; the call allocates nothing.
+ * Its device address is looked up on the first call on each device (with
+ * that device current).  Nothing in it has to start at zero: every call
+ * writes what it reads.  All calls on one device share the array, so calls
+ * that overlap in time on one device (two streams, or a launch still running
+ * when the next is enqueued on another stream) race and corrupt each other's
+ * results; calls in order on one stream are safe.
+ *
+ *  stream   a stream of the current device (or NULL); PA_ERR_INVALID_ARG if
+ *           it belongs to another device.
+ * Returns PA_ERR_SCRATCH, launching nothing, when the call would need more
+ * than PA_NOALLOC_SCRATCH_BYTES (pa_decode_workspace_size gives the need),
+ * The balanced split always fits when num_heads * (head_size + 4) <= 16256
+ * (up to 64 heads of 128, any num_seqs it takes); the fixed split when
+ * num_seqs * num_heads * partitions * (head_size + 4) * 4 <= 32 MiB.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int paged_attention_decode_noalloc(void* out, const void* query, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                                   int block_size, int max_blocks_per_seq, int num_blocks,
+                                   int max_seq_len, float scale, int dtype, int partition_size,
+                                   unsigned flags, void* stream);
 
 /*
  * Several new tokens per sequence, attending causally over the paged cache

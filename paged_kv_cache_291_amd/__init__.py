@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     PA_ERR_CAPACITY,
     PA_ERR_INVALID_ARG,
     PA_ERR_NO_BLOCKS,
+    PA_ERR_SCRATCH,
     PA_FLAG_SHARED_BLOCKS,
     PA_FP8_E4M3,
     BlockManager,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     pa_prefill_workspace_size,
     pa_status_string,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_decode_fp8,
     paged_attention_prefill,
     reshape_and_cache,

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 0, -1, -2, -3, -4
-PA_ERR_NO_BLOCKS, PA_ERR_CAPACITY = -5, -6
+PA_ERR_NO_BLOCKS, PA_ERR_CAPACITY, PA_ERR_SCRATCH = -5, -6, -7
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_FLAG_SHARED_BLOCKS = 1
 DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -26,6 +26,7 @@ DTYPE_CODES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 FP8_POOL_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 EXPORTED = ("pa_status_string", "pa_decode_workspace_size", "paged_attention_decode", "reshape_and_cache",
+            "paged_attention_decode_noalloc",
             "paged_attention_decode_fp8", "reshape_and_cache_fp8", "paged_attention_prefill",
             "paged_attention_prefill_fp8", "pa_prefill_workspace_size",
             "copy_blocks", "pa_bm_create", "pa_bm_destroy", "pa_bm_allocate", "pa_bm_append_slots", "pa_bm_fork",
@@ -60,6 +61,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
                                            c_int, c_int, c_int, c_float, c_int, c_int, ctypes.c_uint, vp,
                                            c_size, vp]
+    lib.paged_attention_decode_noalloc.restype = c_int
+    lib.paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
+                                                   c_int, c_int, c_int, c_float, c_int, c_int, ctypes.c_uint, vp]
     lib.reshape_and_cache.restype = c_int
     lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int, vp]
     lib.paged_attention_decode_fp8.restype = c_int
@@ -187,6 +191,31 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
         _dev(seq_lens, "seq_lens", torch.int32), S, Hq, Hkv, D, BS, block_tables.shape[1], NB,
         int(max_seq_len), float(scale), DTYPE_CODES[dt], int(partition_size), int(flags), ws_ptr, ws_bytes,
         _stream(stream))
+    _check(rc)
+    return out
+
+
+def paged_attention_decode_noalloc(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                   scale: float, partition_size: int = 0, max_seq_len: int = 0, flags: int = 0,
+                                   stream=None) -> torch.Tensor:
+    """``paged_attention_decode`` with the library's own device scratch array
+    in place of a workspace: nothing is allocated (see
+    ``include/pagedattn.h``; calls that overlap in time on one device race)."""
+    S, Hq, D = query.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    if tuple(out.shape) != (S, Hq, D) or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between out/query/k_cache/v_cache")
+    if query.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported dtype {query.dtype}")
+    dt = query.dtype
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and seq_lens [S]")
+    rc = load_library().paged_attention_decode_noalloc(
+        _dev(out, "out", dt), _dev(query, "query", dt), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), _dev(block_tables, "block_tables", torch.int32),
+        _dev(seq_lens, "seq_lens", torch.int32), S, Hq, Hkv, D, BS, block_tables.shape[1], NB,
+        int(max_seq_len), float(scale), DTYPE_CODES[dt], int(partition_size), int(flags), _stream(stream))
     _check(rc)
     return out
 

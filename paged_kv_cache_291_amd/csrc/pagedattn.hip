@@ -17,6 +17,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pagedattn.h"
 #include "common.h"
 #include "decode_mfma.h"
@@ -301,6 +304,7 @@ extern "C" const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "HIP launch error";
     case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     case PA_ERR_CAPACITY: return "block table full";
+    case PA_ERR_SCRATCH: return "request exceeds the library's fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -313,14 +317,66 @@ extern "C" size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head
   return pa::split_workspace_bytes(num_seqs, num_heads, head_size, np);
 }
 
+// Device memory of paged_attention_decode_noalloc: it stands in for the
+// caller's workspace.  Each device the library runs on holds its own copy
+// until the process ends; every call on a device shares it.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 namespace pa {
 namespace {
+
+constexpr int kScratchMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchMaxDevices];   // per device, found once with that device current
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array (the host-side name
+// of the array is only a stand-in, never a device address).  The stream, if
+// not the null stream, must belong to the current device.
+int scratch_address(void* stream, void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kScratchMaxDevices) return PA_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return PA_ERR_HIP;
+    if (sdev != dev) return PA_ERR_INVALID_ARG;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PA_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return PA_OK;
+}
+
+// Partitions per sequence of the fixed split: max_seq_len, or the table
+// row's capacity when 0 is passed, in partition_size pieces.
+int split_num_parts(int block_size, int max_blocks_per_seq, int max_seq_len, int partition_size) {
+  const long long cap = (long long)max_blocks_per_seq * block_size;
+  const int msl = max_seq_len > 0 ? max_seq_len : (int)(cap < 0x7fffffffLL ? cap : 0x7fffffffLL);
+  return msl > 0 ? ceil_div(msl, partition_size) : 1;
+}
+
+// Workspace bytes a decode call with these (already validated) sizes uses.
+size_t decode_workspace_need(int num_seqs, int num_heads, int head_size, int block_size, int max_blocks_per_seq,
+                             int max_seq_len, int partition_size, int dtype) {
+  if (partition_size > 0)
+    return split_workspace_bytes(num_seqs, num_heads, head_size,
+                                 split_num_parts(block_size, max_blocks_per_seq, max_seq_len, partition_size));
+  return dtype != PA_F32 ? balanced_workspace_bytes(num_seqs, num_heads, head_size) : 0;
+}
 
 int decode_impl(void* out, const void* query, const void* k_cache, const void* v_cache,
                 const int32_t* block_tables, const int32_t* seq_lens, int num_seqs, int num_heads,
                 int num_kv_heads, int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
                 int max_seq_len, float scale, int dtype, int partition_size, unsigned flags, void* workspace,
-                size_t workspace_bytes, void* stream, bool fp8_kv, float k_scale, float v_scale) {
+                size_t workspace_bytes, void* stream, bool fp8_kv, float k_scale, float v_scale,
+                bool noalloc = false) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 ||
       max_blocks_per_seq < 0 || num_blocks < 0 || max_seq_len < 0 || partition_size < 0)
     return PA_ERR_INVALID_ARG;
@@ -339,6 +395,16 @@ int decode_impl(void* out, const void* query, const void* k_cache, const void* v
   const int kv_bytes = fp8_kv ? 1 : elem_bytes(dtype);
   if ((long long)kBlockSize * num_kv_heads * head_size * kv_bytes > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
 
+  const size_t need = decode_workspace_need(num_seqs, num_heads, head_size, block_size, max_blocks_per_seq,
+                                            max_seq_len, partition_size, dtype);
+  if (partition_size == 0 && dtype != PA_F32 && num_seqs > kSkMaxSeqs) return PA_ERR_UNSUPPORTED;
+  if (noalloc && need > 0) {                  // the library's scratch array in place of a workspace
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+    const int rc = scratch_address(stream, &workspace);
+    if (rc != PA_OK) return rc;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
+
   Args a{};
   a.out = out; a.query = query;
   a.kc = static_cast<const char*>(k_cache); a.vc = static_cast<const char*>(v_cache);
@@ -350,16 +416,9 @@ int decode_impl(void* out, const void* query, const void* k_cache, const void* v
   a.fp8_kv = fp8_kv;
   a.part_tokens = 0; a.num_parts = 1;
   a.stream_kv = (flags & PA_FLAG_SHARED_BLOCKS) == 0;
-  size_t need = 0;
   if (partition_size > 0) {
-    const long long cap = (long long)max_blocks_per_seq * block_size;
-    const int msl = max_seq_len > 0 ? max_seq_len : (int)(cap < 0x7fffffffLL ? cap : 0x7fffffffLL);
     a.part_tokens = partition_size;
-    a.num_parts = msl > 0 ? ceil_div(msl, partition_size) : 1;
-    need = split_workspace_bytes(num_seqs, num_heads, head_size, a.num_parts);
-  } else if (dtype != PA_F32) {
-    if (num_seqs > kSkMaxSeqs) return PA_ERR_UNSUPPORTED;
-    need = balanced_workspace_bytes(num_seqs, num_heads, head_size);
+    a.num_parts = split_num_parts(block_size, max_blocks_per_seq, max_seq_len, partition_size);
   }
   if (need > 0) {
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return PA_ERR_WORKSPACE;
@@ -534,6 +593,18 @@ extern "C" int paged_attention_decode(void* out, const void* query, const void* 
   return pa::decode_impl(out, query, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                          head_size, block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale, dtype,
                          partition_size, flags, workspace, workspace_bytes, stream, false, 1.0f, 1.0f);
+}
+
+extern "C" int paged_attention_decode_noalloc(void* out, const void* query, const void* k_cache,
+                                              const void* v_cache, const int32_t* block_tables,
+                                              const int32_t* seq_lens, int num_seqs, int num_heads,
+                                              int num_kv_heads, int head_size, int block_size,
+                                              int max_blocks_per_seq, int num_blocks, int max_seq_len, float scale,
+                                              int dtype, int partition_size, unsigned flags, void* stream) {
+  if (dtype == PA_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  return pa::decode_impl(out, query, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                         head_size, block_size, max_blocks_per_seq, num_blocks, max_seq_len, scale, dtype,
+                         partition_size, flags, nullptr, 0, stream, false, 1.0f, 1.0f, true);
 }
 
 extern "C" int paged_attention_decode_fp8(void* out, const void* query, const void* k_cache, const void* v_cache,

@@ -90,6 +90,39 @@ def test_decode_host_errors():
     assert _decode(lib, **p2) == -1                              # misaligned query
 
 
+def _decode_noalloc(lib, **kw):
+    a = dict(out=None, q=None, kc=None, vc=None, bt=None, sl=None, S=4, Hq=8, Hkv=8, D=64, BS=16,
+             MB=4, NB=64, msl=0, scale=0.125, dtype=2, ps=0, flags=0, stream=None)
+    a.update(kw)
+    return lib.paged_attention_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["S"],
+                                              a["Hq"], a["Hkv"], a["D"], a["BS"], a["MB"], a["NB"], a["msl"],
+                                              a["scale"], a["dtype"], a["ps"], a["flags"], a["stream"])
+
+
+def test_decode_noalloc_host_errors():
+    """The allocation-free decode checks its arguments like
+    paged_attention_decode, and refuses (before any device call) a call
+    whose workspace need exceeds its 32 MiB scratch array."""
+    lib = P.load_library()
+    ptrs = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE)
+    assert _decode_noalloc(lib) == -1                            # null pointers
+    assert _decode_noalloc(lib, S=0) == 0
+    assert _decode_noalloc(lib, dtype=3, **ptrs) == -1           # fp8 pools have their own entry point
+    assert _decode_noalloc(lib, D=96, **ptrs) == -2
+    assert _decode_noalloc(lib, ps=24, **ptrs) == -1
+    assert _decode_noalloc(lib, S=16384, **ptrs) == -2           # more sequences than the balanced split takes
+    # balanced split, 128 heads of 128: 256 * 128 * 2 * 132 * 4 bytes of records > 32 MiB
+    assert P.pa_decode_workspace_size(2, 128, 128, 32, 0) > 32 << 20
+    assert _decode_noalloc(lib, S=2, Hq=128, Hkv=16, D=128, MB=2, msl=32, **ptrs) == -7
+    # 64 heads of 128 fit at the balanced split's largest batch
+    assert P.pa_decode_workspace_size(16383, 64, 128, 0, 0) <= 32 << 20
+    # fixed split, 64 sequences x 64 heads x 64 partitions of 512: 138 MB
+    assert _decode_noalloc(lib, S=64, Hq=64, Hkv=8, D=128, MB=2048, msl=32768, ps=512, **ptrs) == -7
+    # max_seq_len 0: the table row's capacity sizes the partitions
+    assert _decode_noalloc(lib, S=64, Hq=64, Hkv=8, D=128, MB=2048, msl=0, ps=512, **ptrs) == -7
+    assert "scratch" in P.pa_status_string(-7)
+
+
 def test_scatter_host_errors():
     lib = P.load_library()
     f = lib.reshape_and_cache
