@@ -32,8 +32,8 @@
 //    size: work items (sequence, partition, head group), up to two per
 //    workgroup.
 //  * pa_prefill_kernel / pa_prefill_lds_kernel: multi-token queries, one
-//    wave per 16-row tile; the LDS variant shares each K/V block among 8
-//    tiles.
+//    wave per 16-row tile; the LDS variant shares each K/V block among the
+//    16 tiles of a workgroup, two per wave.
 #pragma once
 
 #include "common.h"
@@ -286,22 +286,23 @@ __device__ __forceinline__ bool mfma_segment(MfmaState<D>& st, const char* __res
   return false;
 }
 
-// Causal variant for multi-token queries: the 16 rows of the tile are
-// (token, head) pairs with their own last visible position `row_last` (one
-// per lane: this lane's row l%16).  Blocks [b_begin, b_end) of the sequence
-// are streamed; blocks from `mask_from` on are masked per row.  V rows past
-// the sequence's last token `seq_last` are zeroed (they may hold anything);
-// inside the sequence a masked key only needs its zero probability.  A row
-// may see no key of the whole range (a range holding only the sequence's
-// last keys): its max stays -inf and its probabilities and sum stay 0, so
-// a partial result of such a row weighs nothing in the merge.  LOCK as in
-// mfma_segment.
-template <class E, class KV, int D, bool NT, bool LOCK>
-__device__ __forceinline__ bool mfma_segment_rows(MfmaState<D>& st, const char* __restrict__ k_cache,
+// Causal variant for multi-token queries: the 16 rows of each of the NTILE
+// tiles are (token, head) pairs with their own last visible position
+// `row_last[t]` (one per lane and tile: this lane's row l%16).  Blocks
+// [b_begin, b_end) of the sequence are streamed once for all tiles (each
+// loaded block feeds every tile's QK and PV); blocks from `mask_from` on are
+// masked per row.  V rows past the sequence's last token `seq_last` are
+// zeroed (they may hold anything); inside the sequence a masked key only
+// needs its zero probability.  A row may see no key of the whole range (a
+// range holding only the sequence's last keys): its max stays -inf and its
+// probabilities and sum stay 0, so a partial result of such a row weighs
+// nothing in the merge.  LOCK as in mfma_segment.
+template <class E, class KV, int D, bool NT, bool LOCK, int NTILE>
+__device__ __forceinline__ bool mfma_segment_rows(MfmaState<D> (&st)[NTILE], const char* __restrict__ k_cache,
                                                   const char* __restrict__ v_cache, const int* __restrict__ bt_row,
-                                                  int b_begin, int b_end, int mask_from, int row_last, int seq_last,
-                                                  int num_blocks, int num_kv_heads, int kvh, float qk_scale,
-                                                  int lane) {
+                                                  int b_begin, int b_end, int mask_from,
+                                                  const int (&row_last)[NTILE], int seq_last, int num_blocks,
+                                                  int num_kv_heads, int kvh, float qk_scale, int lane) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
   using IO = KvIo<KV, E, D>;
@@ -321,37 +322,41 @@ __device__ __forceinline__ bool mfma_segment_rows(MfmaState<D>& st, const char* 
 
   // key0: position of the block's first key
   auto consume = [&](const Blk& b, int key0, bool masked) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    u32x2 pa[NTILE];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) sc = M::qk(IO::k_operand(b, k), st.qb[k], sc);
-    // lane l holds S[row = l%16][key = key0 + 4*(l/16) + i]; row_last is that row's limit
-    float z[4];
+    for (int t = 0; t < NTILE; ++t) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = sc[i] * qk_scale;
-      if (masked && key0 + 4 * g + i > row_last) z[i] = -INFINITY;
+      for (int k = 0; k < KS; ++k) sc = M::qk(IO::k_operand(b, k), st[t].qb[k], sc);
+      // lane l holds S[row = l%16][key = key0 + 4*(l/16) + i]; row_last is that row's limit
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = sc[i] * qk_scale;
+        if (masked && key0 + 4 * g + i > row_last[t]) z[i] = -INFINITY;
+      }
+      const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      if (__ballot(bm > st[t].m_ref + kRescaleThreshold)) {
+        const float m_new = fmaxf(st[t].m_ref, bm);
+        // 0 on a row's first visible block; a row with nothing visible yet keeps 0 state
+        const float alpha = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[t].m_ref - m_new);
+        st[t].l_part *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int T = 0; T < VE; ++T)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[t].acc[T][i] *= ar[i];
+        st[t].m_ref = m_new;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[i] = (masked && z[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[i] - st[t].m_ref);
+      st[t].l_part += (p[0] + p[1]) + (p[2] + p[3]);
+      pa[t] = u32x2{pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
     }
-    const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-    if (__ballot(bm > st.m_ref + kRescaleThreshold)) {
-      const float m_new = fmaxf(st.m_ref, bm);
-      // 0 on a row's first visible block; a row with nothing visible yet keeps 0 state
-      const float alpha = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
-      st.l_part *= alpha;
-      float ar[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int T = 0; T < VE; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.acc[T][i] *= ar[i];
-      st.m_ref = m_new;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      p[i] = (masked && z[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(z[i] - st.m_ref);
-    st.l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    const u32x2 pa = {pack2<E>(p[0], p[1]), pack2<E>(p[2], p[3])};
     uint32_t v[4][VW];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -362,7 +367,8 @@ __device__ __forceinline__ bool mfma_segment_rows(MfmaState<D>& st, const char* 
       const uint32_t sel = (T & 1) ? 0x07060302u : 0x05040100u;
       const u32x2 vb = {__builtin_amdgcn_perm(v[1][T >> 1], v[0][T >> 1], sel),
                         __builtin_amdgcn_perm(v[3][T >> 1], v[2][T >> 1], sel)};
-      st.acc[T] = M::pv(pa, vb, st.acc[T]);
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) st[t].acc[T] = M::pv(pa[t], vb, st[t].acc[T]);
     }
   };
 
@@ -598,29 +604,34 @@ __device__ inline void blocks_prefix_sum(const int* __restrict__ seq_lens, int n
 // A workgroup is up to 8 waves; 12 wave slots per CU would still hold only
 // one, so the register budget is that of 2 waves per SIMD.
 // MQ: several query tokens per sequence (query_start[s] .. query_start[s+1]),
-// at most 16 * tiles / G; the workgroup has `tiles` waves per kv head (wave
-// = tile * hpw + head), wave (t, h) taking rows 16t .. 16t + 15 of head h's
-// (token, head) pairs.  The waves of one kv head read the same K/V rows in
-// step, so HBM sees them once.  The sequence's final blocks are masked per
-// row (causal), partial records hold 16 * tiles rows per kv head, and
-// pa_sk_merge_mq_kernel merges them.
-template <class E, class KV, int D, int G, bool NT, bool MQ = false>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// at most 16 * TILES / G: the wave of a kv head holds TILES 16-row tiles of
+// its (token, head) pairs (tile t: rows 16t .. 16t + 15) and feeds each
+// loaded block to all of them, so every K/V line is read once.  The
+// sequence's final blocks are masked per row (causal), partial records hold
+// 16 * TILES rows per kv head, and pa_sk_merge_mq_kernel merges them.
+// Two 16-row tiles of 128-wide heads need more than the 256 registers of two
+// waves per SIMD: that launch gives each wave a SIMD of its own (at most 4
+// kv heads per workgroup).
+template <int D, int TILES> constexpr bool sk_wide() { return TILES == 2 && D == 128; }
+constexpr int kSkWideHeads = 4;
+
+template <class E, class KV, int D, int G, bool NT, bool MQ = false, int TILES = 1>
+__global__ void __launch_bounds__((sk_wide<D, TILES>() ? 64 * kSkWideHeads : 512))
+__attribute__((amdgpu_waves_per_eu(sk_wide<D, TILES>() ? 1 : 2, sk_wide<D, TILES>() ? 1 : 8)))
 pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
                     const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                     const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                     int num_seqs, int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
                     float qk_scale, float v_scale, int hpw, int nwg, int4* __restrict__ ws_seq,
-                    float* __restrict__ ws_rec, const int* __restrict__ query_start = nullptr, int tiles = 1) {
+                    float* __restrict__ ws_rec, const int* __restrict__ query_start = nullptr) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
-  const int RPK = MQ ? 16 * tiles : G;         // record rows per kv head and slot
+  constexpr int RPK = MQ ? 16 * TILES : G;     // record rows per kv head and slot
   extern __shared__ int s_cum[];
   __shared__ int s_wsum[16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int hg = blockIdx.x / nwg, rank = blockIdx.x - hg * nwg;
-  const int tile = wave / hpw, wv = wave - tile * hpw;   // MQ: 16-row tile of the kv head's rows
   const int kvh = hg * hpw + wv;
 
   blocks_prefix_sum(seq_lens, num_seqs, max_blocks, s_cum, s_wsum);
@@ -646,7 +657,7 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     if (s_cum[s + 1] != s_cum[s]) continue;
     if (hg == 0 && tid == 0) ws_seq[s] = int4{-1, 0, 0, U};
     if constexpr (MQ) {                        // query rows of a sequence without blocks break the contract
-      const int a = s_qs[s], nq = tile == 0 ? s_qs[s + 1] - a : 0;
+      const int a = s_qs[s], nq = s_qs[s + 1] - a;
       for (int t = 0; t < nq; ++t) {
         const int64_t e0 = ((int64_t)(a + t) * num_heads + kvh * G) * D;
         for (int i = lane; i < G * D; i += 64) store_elem<E>(out, e0 + i, qnan());
@@ -666,13 +677,13 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     if (s_cum[mid] <= u0) lo = mid; else hi = mid;
   }
   int s = lo;
-  float* rec_wg = ws_rec + (((int64_t)blockIdx.x * 2 * hpw + wv) * RPK + (MQ ? 16 * tile : 0)) * REC;
+  float* rec_wg = ws_rec + ((int64_t)blockIdx.x * 2 * hpw + wv) * RPK * REC;
   // The record of a first segment that ends inside the range is held in
   // registers and written after the range's last segment: records written
   // early are flushed to HBM in the middle of the K/V stream (4 rows per
   // wave: 8B batch 248.8 -> 245.0 us; 16 rows per wave, where the records
   // outgrow an XCD's L2: 288 -> 260 us).
-  MfmaState<D> held;
+  MfmaState<D> held[MQ ? TILES : 1];
   bool held_bad = false, have_held = false;
   int held_a = 0, held_nq = 0;
   int64_t held_row0 = 0;
@@ -687,26 +698,37 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
       const int a = s_qs[s], nq = s_qs[s + 1] - a;
       if (nq > 0) {                            // same for every wave of the workgroup
         const int g = lane >> 4, c = lane & 15;
-        const int t0 = 16 * tile / G;          // first token of this wave's tile (its rows may all be past nq:
-                                               // the wave still streams the blocks, in step with the others)
-        const int tok = t0 + c / G;
-        const bool live = tok < nq;
-        MfmaState<D> st;
-        mfma_begin_row<KV, D>(st, query, (int64_t)(a + (live ? tok : 0)) * num_heads + kvh * G + c % G, live, g);
-        const int row_last = L - nq + min(tok, nq - 1);
+        MfmaState<D> st[TILES];
+        int row_last[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {      // tile t: tokens 16t/G + r/G (rows past nq are padding)
+          const int tok = 16 * t / G + c / G;
+          const bool live = tok < nq;
+          mfma_begin_row<KV, D>(st[t], query, (int64_t)(a + (live ? tok : 0)) * num_heads + kvh * G + c % G, live,
+                                g);
+          row_last[t] = L - nq + min(tok, nq - 1);
+        }
         bool bad = nq > L;
         if (!bad)
-          bad = mfma_segment_rows<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
-                                                      b0, b1, (L - nq + 1) / BS, row_last, L - 1, num_blocks,
-                                                      num_kv_heads, kvh, qk_scale, lane);
-        if (u == u0 && rec != nullptr && c1 < u1) {     // first segment, not the range's last
-          held = st;
+          bad = mfma_segment_rows<E, KV, D, NT, true, TILES>(st, k_cache, v_cache,
+                                                             block_tables + (int64_t)s * max_blocks, b0, b1,
+                                                             (L - nq + 1) / BS, row_last, L - 1, num_blocks,
+                                                             num_kv_heads, kvh, qk_scale, lane);
+        const bool hold = u == u0 && rec != nullptr && c1 < u1;      // first segment, not the range's last
+        if (hold) {
+#pragma unroll
+          for (int t = 0; t < TILES; ++t) held[t] = st[t];
           held_bad = bad;
-          held_a = a + t0;
-          held_nq = nq - t0;
+          held_a = a;
+          held_nq = nq;
           have_held = true;
         } else {
-          mfma_finish_rows<E, D, G>(st, bad, out, a + t0, nq - t0, num_heads, kvh, rec, REC, v_scale, lane);
+#pragma unroll
+          for (int t = 0; t < TILES; ++t) {
+            const int t0 = 16 * t / G;
+            mfma_finish_rows<E, D, G>(st[t], bad, out, a + t0, nq - t0, num_heads, kvh,
+                                      rec != nullptr ? rec + 16 * t * REC : nullptr, REC, v_scale, lane);
+          }
         }
       }
     } else {
@@ -717,7 +739,7 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
                                                         b0, b1, min(L, b1 * BS), num_blocks, num_kv_heads, kvh,
                                                         qk_scale, lane);
       if (u == u0 && rec != nullptr && c1 < u1) {
-        held = st;
+        held[0] = st;
         held_bad = bad;
         held_row0 = row0;
         have_held = true;
@@ -729,10 +751,16 @@ pa_decode_sk_kernel(void* __restrict__ out, const void* __restrict__ query,
     ++s;
   }
   if (have_held) {
-    if constexpr (MQ)
-      mfma_finish_rows<E, D, G>(held, held_bad, out, held_a, held_nq, num_heads, kvh, rec_wg, REC, v_scale, lane);
-    else
-      mfma_finish<E, D, G>(held, held_bad, out, held_row0, rec_wg, REC, v_scale, lane);
+    if constexpr (MQ) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const int t0 = 16 * t / G;
+        mfma_finish_rows<E, D, G>(held[t], held_bad, out, held_a + t0, held_nq - t0, num_heads, kvh,
+                                  rec_wg + 16 * t * REC, REC, v_scale, lane);
+      }
+    } else {
+      mfma_finish<E, D, G>(held[0], held_bad, out, held_row0, rec_wg, REC, v_scale, lane);
+    }
   }
 }
 
@@ -764,16 +792,17 @@ pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const 
   // this lane's row c: token tok0 + c/G (padding rows past n reuse the last token's limit)
   const int my_tok = tok0 + c / G;
   const bool row_live = my_tok < n;
-  MfmaState<D> st;
+  MfmaState<D> sts[1];
+  MfmaState<D>& st = sts[0];
   mfma_begin_row<KV, D>(st, query, (int64_t)(q0 + (row_live ? my_tok : 0)) * num_heads + kvh * G + c % G, row_live, g);
   bool bad = bad_len;
   if (!bad_len) {
     const int first_pos = L - n + tok0;                          // the tile's smallest limit
     const int last_pos = L - n + min(tok0 + TPT, n) - 1;          // and largest
-    const int row_last = L - n + min(my_tok, n - 1);
-    bad = mfma_segment_rows<E, KV, D, NT, false>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks, 0,
-                                                  last_pos / BS + 1, (first_pos + 1) / BS, row_last, L - 1,
-                                                  num_blocks, num_kv_heads, kvh, qk_scale, lane);
+    const int row_last[1] = {L - n + min(my_tok, n - 1)};
+    bad = mfma_segment_rows<E, KV, D, NT, false, 1>(sts, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
+                                                     0, last_pos / BS + 1, (first_pos + 1) / BS, row_last, L - 1,
+                                                     num_blocks, num_kv_heads, kvh, qk_scale, lane);
   }
   // rows r = 4*(l/16) + i of the accumulator: token tok0 + r/G, head r%G
   const float l_row = rows_sum(st.l_part);
@@ -817,28 +846,34 @@ __device__ inline u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Query tiles per wave of pa_prefill_lds_kernel (a workgroup covers 8x as many).
+// Query tiles of one pa_prefill_lds_kernel workgroup, and per wave: 16
+// tiles per workgroup, TW per wave (2: 8 waves, two per SIMD; 4: 4 waves, one
+// per SIMD with the accumulators in AGPRs).
+constexpr int kPfTilesPerGroup = 16;
 constexpr int kPfTilesPerWave = 2;
 
-// Grid: one workgroup of 8 waves per (sequence, kv head, 16 consecutive query
-// tiles); wave w owns tiles 16*grp + 2w and 2w + 1 (16 (token, head) rows
-// each, as in pa_prefill_kernel).  The workgroup streams the sequence's
-// blocks in stages of kPfStageBlocks, double-buffered in LDS with one barrier
-// per stage: wave w copies blocks w%4 + 4j of the next stage, K (w < 4) or V
-// (w >= 4), while every wave consumes the current stage's blocks it can see,
-// two blocks per step, both of its tiles on each operand read from LDS:
-//   QK: two 16-key score tiles (16x16x32 MFMAs over head_size);
+// Grid: one workgroup of 16 / TW waves per (sequence, kv head, 16
+// consecutive query tiles); wave w owns tiles 16*grp + TW*w .. TW*w + TW - 1
+// (16 (token, head) rows each, as in pa_prefill_kernel).  The workgroup
+// streams the sequence's blocks in stages of kPfStageBlocks, double-buffered
+// in LDS with one barrier per stage: the waves copy the next stage's K and V
+// blocks (8 waves: one block of K (w < 4) or V each; 4 waves: block w of K
+// and of V), while every wave consumes the current stage's blocks it can see,
+// two blocks per step, all of its tiles on each operand read from LDS:
+//   QK: TW 16-key score tiles per block (16x16x32 MFMAs over head_size);
 //   PV: one 16x16x32 MFMA per 16 output columns over the pair's 32 keys, and
 //       one more against a column of ones, which sums each row's weights as
 //       rounded for the PV step (the softmax denominator).
 // Each K/V byte is read from memory once per 16 tiles instead of once per
-// tile.  Rows past the sequence end, blocks past the workgroup's last block
-// and out-of-pool block ids load as zeros (the buffer range of the block is
-// cut to its valid rows).  The linear workgroup id is split so that all
-// workgroups of one (sequence, kv head) land on the same XCD (workgroups are
-// dealt to the 8 XCDs round robin), where its K/V stay in that XCD's L2.
-template <class E, class KV, int D, int G, bool NT>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// tile, and from LDS once per TW tiles.  Rows past the sequence end, blocks
+// past the workgroup's last block and out-of-pool block ids load as zeros
+// (the buffer range of the block is cut to its valid rows).  The linear
+// workgroup id is split so that all workgroups of one (sequence, kv head)
+// land on the same XCD (workgroups are dealt to the 8 XCDs round robin),
+// where its K/V stay in that XCD's L2.
+template <class E, class KV, int D, int G, bool NT, int TW>
+__global__ void __launch_bounds__(64 * kPfTilesPerGroup / TW)
+__attribute__((amdgpu_waves_per_eu(TW == 4 ? 1 : 2, TW == 4 ? 1 : 8)))
 pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, const char* __restrict__ k_cache,
                       const char* __restrict__ v_cache, const int* __restrict__ block_tables,
                       const int* __restrict__ seq_lens, const int* __restrict__ query_start, int num_seqs,
@@ -846,15 +881,16 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
                       float qk_scale, float v_scale) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
-  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe, TW = kPfTilesPerWave;
-  static_assert(TW == 2, "the pipelined step interleaves exactly two tiles");
+  constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe;
+  constexpr int WAVES = kPfTilesPerGroup / TW;
+  static_assert(TW == 2 || TW == 4, "two or four tiles per wave");
   constexpr int RP = pf_k_pitch<D>(), VP = pf_v_pitch<D>(), KB = pf_k_bytes<D>(), SB = pf_stage_bytes<D>();
   constexpr int KVB = KV::kBytes;                     // bytes per element in the pools
   constexpr int CPR = D * KVB / 16;                   // 16-byte chunks per pool row
   constexpr int DPC = 16 / KVB;                       // elements per chunk
   constexpr int KC = CPR / 4;                         // chunks per lane and block: 16 rows per block
-  constexpr int SBW = kPfStageBlocks / 4;             // blocks of a stage each staging wave copies
-  static_assert(kPfStageBlocks % 4 == 0 && KC >= 1, "stage layout");
+  constexpr int JOBS = 2 * kPfStageBlocks / WAVES;    // blocks (of K or V) each wave copies per stage
+  static_assert(kPfStageBlocks == 4 && KC >= 1, "stage layout");
   __shared__ __align__(16) char smem[2 * SB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -864,7 +900,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   if (pair >= num_seqs * num_kv_heads) return;
   const int s = pair / num_kv_heads, kvh = pair - s * num_kv_heads;
   const int q0 = query_start[s], n = query_start[s + 1] - q0, L = seq_lens[s];
-  const int wg_tok0 = grp * 8 * TW * TPT;
+  const int wg_tok0 = grp * kPfTilesPerGroup * TPT;
   if (n <= 0 || wg_tok0 >= n) return;                // the whole workgroup: uniform
   const bool bad_len = n > L || (int64_t)L > (int64_t)max_blocks * BS;
 
@@ -896,17 +932,16 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   const int my_b_end = active ? my_last / BS + 1 : 0;
   const int my_p_end = (my_b_end + 1) / 2;            // block pairs this wave consumes
   const int my_p_open = ((my_first + 1) / BS) / 2;    // pairs before this one are visible to every row
-  const int wg_last = L - n + min(wg_tok0 + 8 * TW * TPT, n) - 1;
+  const int wg_last = L - n + min(wg_tok0 + kPfTilesPerGroup * TPT, n) - 1;
   const int wg_b_end = bad_len ? 0 : wg_last / BS + 1;
   const int* bt_row = block_tables + (int64_t)s * max_blocks;
 
-  // staging role of this wave: blocks sblk + 4j of every stage, K or V
-  const bool v_role = wave >= 4;
+  // staging jobs of this wave: block sblk of every stage, of K and/or V
   const int sblk = wave & 3;
+  auto v_job = [&](int j) { return WAVES == 4 ? j == 1 : wave >= 4; };   // j is unrolled: folds for 4 waves
   const int row_stride = num_kv_heads * D * KVB;
   const int blk_bytes = BS * row_stride;
   const int head_off = kvh * D * KVB;
-  const char* pool = v_role ? v_cache : k_cache;
   int voff[KC];
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
@@ -914,7 +949,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
     voff[i] = (q / CPR) * row_stride + head_off + (q % CPR) * 16;
   }
 
-  u32x4 regs[SBW][KC];
+  u32x4 regs[JOBS][KC];
   int ids = 0;                                        // block ids of the current window of 64 blocks
   bool bad_id = false;
   auto issue = [&](int stage) {
@@ -923,12 +958,13 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
       ids = idx < wg_b_end ? bt_row[idx] : 0;
       bad_id |= __ballot(idx < wg_b_end && (unsigned)ids >= (unsigned)num_blocks) != 0;
     }
+    const int bi = stage * kPfStageBlocks + sblk;
+    const int id = __builtin_amdgcn_readlane(ids, bi & 63);
+    const bool ok = bi < wg_b_end && (unsigned)id < (unsigned)num_blocks;
+    const int rows = ok ? min(BS, L - bi * BS) : 0;
 #pragma unroll
-    for (int j = 0; j < SBW; ++j) {
-      const int bi = stage * kPfStageBlocks + sblk + 4 * j;
-      const int id = __builtin_amdgcn_readlane(ids, bi & 63);
-      const bool ok = bi < wg_b_end && (unsigned)id < (unsigned)num_blocks;
-      const int rows = ok ? min(BS, L - bi * BS) : 0;
+    for (int j = 0; j < JOBS; ++j) {
+      const char* pool = v_job(j) ? v_cache : k_cache;
       const __amdgpu_buffer_rsrc_t r = block_rsrc(pool + (int64_t)(ok ? id : 0) * blk_bytes, rows * row_stride);
 #pragma unroll
       for (int i = 0; i < KC; ++i) regs[j][i] = load16<NT>(r, voff[i], 0);
@@ -940,22 +976,24 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
     else return (w & 1) ? fp8x2_to<E, true>(x[w >> 1]) : fp8x2_to<E, false>(x[w >> 1]);
   };
   auto commit = [&](int buf) {
-    char* sb = smem + buf * SB + (v_role ? KB : 0);
 #pragma unroll
-    for (int j = 0; j < SBW; ++j)
+    for (int j = 0; j < JOBS; ++j) {
+      const bool vr = v_job(j);
+      char* sb = smem + buf * SB + (vr ? KB : 0);
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
         const int q = lane + 64 * i;
-        char* dst = sb + ((sblk + 4 * j) * BS + q / CPR) * (v_role ? VP : RP) + (q % CPR) * DPC * 2;
+        char* dst = sb + (sblk * BS + q / CPR) * (vr ? VP : RP) + (q % CPR) * DPC * 2;
         const u32x4& x = regs[j][i];
 #pragma unroll
         for (int h = 0; h < DPC / 8; ++h)
           *reinterpret_cast<u32x4*>(dst + 16 * h) =
               u32x4{word(x, 4 * h), word(x, 4 * h + 1), word(x, 4 * h + 2), word(x, 4 * h + 3)};
       }
+    }
   };
 
-  // A step covers blocks 2p, 2p+1 of a stage for both tiles (key0: position
+  // A step covers blocks 2p, 2p+1 of a stage for all tiles (key0: position
   // of block 2p's first key), in three parts: scores (QK and the row maxima),
   // rescale (rare: one branch for both tiles) and weights_pv (exponentials
   // and PV).  Every row sees key 0, and the first pair is consumed before any
@@ -1082,7 +1120,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
     // pairs every row sees, software-pipelined: the exponentials and PV of
     // one pair and the QK and maxima of the next form one scheduling region,
     // ordered so that each group of vector instructions has matrix-core work
-    // of the other tile or pair beside it
+    // of another tile or pair beside it
     if (p_lo < p_mid) {
       Scores cur;
       {
@@ -1102,14 +1140,14 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
         u32x4 vb[VE];
         v_read(sbuf, p - p_lo, vb);
         k_read(sbuf, p + 1 - p_lo, x);
-        const u32x4 pa0 = weights(std::false_type{}, 0, cur);
-        qk(0, x, nxt);
-        pv(0, pa0, vb);
-        const u32x4 pa1 = weights(std::false_type{}, 1, cur);
-        qk(1, x, nxt);
-        maxima(std::false_type{}, 0, 0, nxt);
-        pv(1, pa1, vb);
-        maxima(std::false_type{}, 1, 0, nxt);
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          const u32x4 pa = weights(std::false_type{}, t, cur);
+          qk(t, x, nxt);
+          if (t > 0) maxima(std::false_type{}, t - 1, 0, nxt);
+          pv(t, pa, vb);
+        }
+        maxima(std::false_type{}, TW - 1, 0, nxt);
         cur = nxt;
       }
       rescale(cur);

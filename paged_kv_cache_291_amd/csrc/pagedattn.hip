@@ -166,29 +166,22 @@ size_t balanced_mq_workspace_bytes(int num_seqs, int num_kv_heads, int head_size
 constexpr int kMergeQuadMinSeqs = 64;
 int merge_rows_per_wave(int num_seqs) { return num_seqs >= kMergeQuadMinSeqs ? 4 : 1; }
 
-// Largest divisor of num_kv_heads that is at most 8: kv heads per workgroup.
-int heads_per_workgroup(int num_kv_heads) {
-  for (int d = 8; d > 1; --d)
+// Largest divisor of num_kv_heads that is at most `most` (8: one wave per kv
+// head, two waves per SIMD): kv heads per workgroup.
+int heads_per_workgroup(int num_kv_heads, int most = 8) {
+  for (int d = most; d > 1; --d)
     if (num_kv_heads % d == 0) return d;
   return 1;
 }
 
 // Multi-token queries on the balanced split: 16-row tiles per kv head (the
-// kv head's max_q * G (token, head) rows), at most kSkMaxTiles, and kv heads
-// per workgroup (a divisor of num_kv_heads, with heads * tiles <= 8 waves).
-// 8B batch, 32/8 heads: 5..8 query tokens (2 tiles) 360-370 us here against
-// 390-400 us in the LDS kernel; 12 tokens (3 tiles) 474 vs 411 us, 16 tokens
-// 577 vs 418 us, so 3 and more tiles take the LDS kernel.
+// kv head's max_q * G (token, head) rows), at most kSkMaxTiles; one wave per
+// kv head holds them all (kv heads per workgroup as in decode).
 constexpr int kSkMaxTiles = 2;
 int mq_tiles(int num_heads, int num_kv_heads, int max_q) {      // kSkMaxTiles + 1: more than the split takes
   const long long rows = (long long)max_q * (num_heads / num_kv_heads);
   if (rows > 16LL * kSkMaxTiles) return kSkMaxTiles + 1;
   return rows > 0 ? (int)((rows + 15) / 16) : 1;
-}
-int mq_heads_per_workgroup(int num_kv_heads, int tiles) {
-  for (int d = 8 / tiles; d > 1; --d)
-    if (num_kv_heads % d == 0) return d;
-  return 1;
 }
 
 struct Args {
@@ -442,14 +435,15 @@ int launch_prefill(void* out, const void* query, const void* kc, const void* vc,
   const int tiles = ceil_div(max_query_len * G, 16);
   if (tiles >= kPrefillLdsTiles) {
     // many query tiles per (sequence, kv head): the tiles of a workgroup share K/V through LDS
-    const int gpp = ceil_div(tiles, 8 * kPfTilesPerWave);
+    const int gpp = ceil_div(tiles, kPfTilesPerGroup);
     const long long pairs = (long long)num_seqs * num_kv_heads;
     const long long grid = (pairs + 7) / 8 * 8 * gpp;
     if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    auto k = nt ? pa_prefill_lds_kernel<E, KV, D, G, true> : pa_prefill_lds_kernel<E, KV, D, G, false>;
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(512), 0, st, out, query, static_cast<const char*>(kc),
-                       static_cast<const char*>(vc), bt, sl, qs, num_seqs, num_heads, num_kv_heads, max_blocks,
-                       num_blocks, gpp, qk_scale, v_scale);
+    constexpr int TW = kPfTilesPerWave;
+    auto k = nt ? pa_prefill_lds_kernel<E, KV, D, G, true, TW> : pa_prefill_lds_kernel<E, KV, D, G, false, TW>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * kPfTilesPerGroup / TW), 0, st, out, query,
+                       static_cast<const char*>(kc), static_cast<const char*>(vc), bt, sl, qs, num_seqs, num_heads,
+                       num_kv_heads, max_blocks, num_blocks, gpp, qk_scale, v_scale);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   const dim3 grid((unsigned)ceil_div(tiles, 4), (unsigned)num_seqs, (unsigned)num_kv_heads);
@@ -479,20 +473,18 @@ int launch_mq_split(void* out, const void* query, const void* kc, const void* vc
                     int max_blocks, int num_blocks, int max_q, float qk_scale, float v_scale, bool nt, void* ws,
                     hipStream_t st) {
   const int tiles = mq_tiles(num_heads, num_kv_heads, max_q);
-  const int hpw = mq_heads_per_workgroup(num_kv_heads, tiles);
+  const int hpw = heads_per_workgroup(num_kv_heads, tiles == 2 && sk_wide<D, 2>() ? kSkWideHeads : 8);
   const int groups = num_kv_heads / hpw;
   const int nwg = kSkWorkgroups / groups > 0 ? kSkWorkgroups / groups : 1;
   int4* ws_seq = static_cast<int4*>(ws);
   float* ws_rec = reinterpret_cast<float*>(static_cast<char*>(ws) + balanced_seq_bytes(num_seqs));
   const size_t lds = (size_t)2 * (num_seqs + 1) * sizeof(int);
-  // Several tile waves read each K/V line: the default cache policy keeps it
-  // in L2 for the later ones (non-temporal loads sent them to HBM again:
-  // 8B batch, 8 query tokens, 472 -> 369 us).
-  const bool stream = nt && tiles == 1;
-  auto k = stream ? pa_decode_sk_kernel<E, KV, D, G, true, true> : pa_decode_sk_kernel<E, KV, D, G, false, true>;
-  hipLaunchKernelGGL(k, dim3((unsigned)(groups * nwg)), dim3(64 * hpw * tiles), lds, st, out, query,
+  // one wave per kv head holds all of its tiles, so each K/V line is read once
+  auto k = tiles == 1 ? (nt ? pa_decode_sk_kernel<E, KV, D, G, true, true, 1> : pa_decode_sk_kernel<E, KV, D, G, false, true, 1>)
+                      : (nt ? pa_decode_sk_kernel<E, KV, D, G, true, true, 2> : pa_decode_sk_kernel<E, KV, D, G, false, true, 2>);
+  hipLaunchKernelGGL(k, dim3((unsigned)(groups * nwg)), dim3(64 * hpw), lds, st, out, query,
                      static_cast<const char*>(kc), static_cast<const char*>(vc), bt, sl, num_seqs, num_heads,
-                     num_kv_heads, max_blocks, num_blocks, qk_scale, v_scale, hpw, nwg, ws_seq, ws_rec, qs, tiles);
+                     num_kv_heads, max_blocks, num_blocks, qk_scale, v_scale, hpw, nwg, ws_seq, ws_rec, qs);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   const int rpw = merge_rows_per_wave(num_seqs);
   const long long grid = (long long)num_seqs * num_kv_heads * ceil_div(max_q * G, rpw);

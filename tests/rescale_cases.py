@@ -164,12 +164,12 @@ def heads_per_workgroup(num_kv_heads: int, waves: int = 8) -> int:
     return 1
 
 
-def balanced_segments(nblk: np.ndarray, num_kv_heads: int, tiles: int = 1):
+def balanced_segments(nblk: np.ndarray, num_kv_heads: int, tiles: int = 1, head_size: int = 128):
     """Per sequence, the [b0, b1) block runs of the balanced split: the
     batch's blocks laid end to end and cut into 256 / head-groups equal
-    ranges (a multi-token call with two tile waves per kv head groups half as
-    many kv heads per workgroup)."""
-    hpw = heads_per_workgroup(num_kv_heads, 8 // tiles)
+    ranges (a head group is up to 8 kv heads; up to 4 when a wave holds two
+    tiles of 128-wide heads)."""
+    hpw = heads_per_workgroup(num_kv_heads, 4 if tiles == 2 and head_size == 128 else 8)
     nwg = max(SPLIT_WORKGROUPS // (num_kv_heads // hpw), 1)
     cum = np.concatenate([[0], np.cumsum(nblk)]).astype(np.int64)
     U = int(cum[-1])

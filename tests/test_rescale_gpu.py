@@ -15,8 +15,8 @@ bound: 1e-2 for bf16 outputs, 2e-3 for fp16 (values are N(0, 1/16), so the
 final rounding stays far inside it).
 
 Paths: decode through the balanced split and a fixed 512-token split;
-multi-token rows through the balanced split with one and two tile waves per
-kv head, the many-tile LDS kernel, and, past the split's sequence limit, the
+multi-token rows through the balanced split with one and two tiles per
+kv-head wave, the many-tile LDS kernel, and, past the split's sequence limit, the
 one-wave-per-tile kernel and the LDS kernel with two tiles; 16-bit and fp8
 pools; a large positive and a large negative score scale.
 """
@@ -169,7 +169,7 @@ def _mq_events(path, case, max_q):
     tiles = -(-max_q * G // 16)
     if path.startswith("split"):
         nblk = RC.valid_blocks(wl.seq_lens, wl.max_blocks_per_seq)
-        segs = RC.balanced_segments(nblk, Hkv, tiles)
+        segs = RC.balanced_segments(nblk, Hkv, tiles, wl.head_size)
         return RC.events_over(case, segs, 1, lambda s: [16 * t // G for t in range(tiles)])
     tpt = 16 // G
     waves = lambda s: list(range(0, nq_of(s), tpt))            # noqa: E731
