@@ -118,7 +118,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  *                 batch's blocks are cut into equal shares over the GPU
  *                 (sequences that straddle a share are merged by a second
  *                 kernel); needs a workspace; at most 16383 sequences.  For
- *                 fp32 one pass per (sequence, kv head), no workspace.
+ *                 fp32 one pass per (sequence, kv head), no workspace; so
+ *                 too for bf16/fp16 with num_heads == num_kv_heads and at
+ *                 least 1024 (sequence, kv head) pairs (the workspace is
+ *                 still required).
  *                 > 0: split context into partitions of this many tokens (a
  *                 multiple of block_size); a second kernel merges partitions
  *                 with log-sum-exp weights.  Needs a workspace.

@@ -1,4 +1,5 @@
-// Paged decode on the vector ALUs (used for fp32 KV).
+// Paged decode on the vector ALUs (fp32 KV, and 16-bit KV with one query
+// head per kv head, where a matrix-core tile would be 1/16 dense).
 //
 // One 64-lane wave (one workgroup) per work item (sequence, kv head, chunk of
 // tokens; with part_tokens == 0 the chunk is the whole sequence):
@@ -47,7 +48,8 @@ struct ValuOccupancy {
 };
 
 // ws: partial records [num_seqs * num_heads * num_parts] (split mode only).
-template <class E, int D, int G>
+// NT: K/V loads with the non-temporal policy (blocks read once per call).
+template <class E, int D, int G, bool NT>
 __global__ void __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(ValuOccupancy<E, D, G>::kWaves, 8)))
 pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
@@ -119,8 +121,8 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(v_cache + (int64_t)phys * blk_bytes, blk_bytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kb[i] = load16<true>(rk, lane_off, i * RPI * row_stride);
-      vb[i] = load16<true>(rv, lane_off, i * RPI * row_stride);
+      kb[i] = load16<NT>(rk, lane_off, i * RPI * row_stride);
+      vb[i] = load16<NT>(rv, lane_off, i * RPI * row_stride);
     }
   };
 

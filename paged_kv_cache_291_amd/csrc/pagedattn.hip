@@ -10,7 +10,8 @@
 // for 64-lane waves, matrix cores and HBM3E:
 //   decode_mfma.h  bf16/fp16 KV on the matrix cores (fixed partitions, or a
 //                  balanced split of the whole batch over the GPU)
-//   decode_valu.h  fp32 KV on the vector ALUs
+//   decode_valu.h  fp32 KV, and 16-bit KV without query-head grouping, on
+//                  the vector ALUs
 //   reduce.h       log-sum-exp merge of partial results
 // The scatter kernel below writes new tokens' K/V rows into their slots.
 
@@ -242,7 +243,8 @@ int launch_valu(const Args& a, hipStream_t st) {
   const long long grid = (long long)a.num_seqs * a.num_parts * a.num_kv_heads;
   if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   float* ws = static_cast<float*>(a.ws);
-  hipLaunchKernelGGL((pa_decode_valu_kernel<E, D, G>), dim3((unsigned)grid), dim3(64), 0, st,
+  auto k = a.stream_kv ? pa_decode_valu_kernel<E, D, G, true> : pa_decode_valu_kernel<E, D, G, false>;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64), 0, st,
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
                      a.num_blocks, a.qk_scale, a.part_tokens, a.num_parts, ws);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
@@ -254,6 +256,15 @@ int launch_valu(const Args& a, hipStream_t st) {
   return PA_OK;
 }
 
+// One query head per kv head (no grouping) leaves the matrix-core tile 1/16
+// dense; there 16-bit pools take the vector-ALU core, one wave per (sequence,
+// kv head[, partition]) (13B-shaped batch, 64 seqs x 40 heads: 254.9 us
+// against 257.1 us for the balanced split on the matrix cores; with 512-token
+// partitions 257.7 against 319.3 us).  Without partitions that needs enough
+// (sequence, kv head) items to keep every CU busy; fewer take the balanced
+// split.
+constexpr long long kValuMhaMinItems = 1024;
+
 template <class E, int D, int G>
 int launch(const Args& a, hipStream_t st) {
   if constexpr (E::kBytes == 4) {
@@ -261,6 +272,10 @@ int launch(const Args& a, hipStream_t st) {
   } else if (a.fp8_kv) {
     return a.stream_kv ? launch_mfma<E, KvFp8, D, G, true>(a, st) : launch_mfma<E, KvFp8, D, G, false>(a, st);
   } else {
+    if constexpr (G == 1) {
+      if (a.part_tokens > 0 || (long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems)
+        return launch_valu<E, D, G>(a, st);
+    }
     return a.stream_kv ? launch_mfma<E, Kv16, D, G, true>(a, st) : launch_mfma<E, Kv16, D, G, false>(a, st);
   }
 }

@@ -82,6 +82,46 @@ def test_sweep_all_outputs(dtype, D, Hq, Hkv, ps):
         assert (g[one, h] == want[h // G]).all()
 
 
+@pytest.mark.parametrize("ps", [0, 16, 512])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+def test_mha_vector_core_sweep(dtype, D, ps):
+    """One query head per kv head over 16-bit pools takes the vector-ALU core
+    (with partitions always; without, from 1024 (sequence, kv head) pairs:
+    here 14 x 80).  Every edge length against the oracle; the shared-blocks
+    flag changes no bit."""
+    seed = zlib.crc32(f"mha-valu-{dtype}-{D}-{ps}".encode()) % 10000
+    wl = W.make_random(seed, len(EDGE_LENS), 80, 80, D, dtype, EDGE_LENS, extra_table_cols=2)
+    assert wl.num_seqs * wl.num_kv_heads >= 1024
+    out, dev = gpu_decode(wl, partition_size=ps)
+    ref = oracle_decode(wl)
+    _, g, _ = errors(out, ref)
+    assert_parity(g, ref, dtype, f"MHA vector core {dtype} D={D} ps={ps}")
+    assert (g[0] == 0).all()
+    shared, _ = gpu_decode(wl, dev, partition_size=ps, flags=P.PA_FLAG_SHARED_BLOCKS)
+    assert torch.equal(shared, out)
+
+
+@pytest.mark.parametrize("ps", [0, 16])
+def test_mha_vector_core_contract_violations(ps):
+    """Out-of-contract lengths and ids on the 16-bit vector-ALU path: NaN
+    rows, every other row right."""
+    lens = [40, 33, 17, 50, 64, 20] * 3
+    wl = W.make_random(32, len(lens), 64, 64, 64, "bf16", lens, pool_factor=2.0, extra_table_cols=1)
+    assert wl.num_seqs * wl.num_kv_heads >= 1024
+    bt, sl = wl.block_tables.copy(), wl.seq_lens.copy()
+    sl[1] = bt.shape[1] * 16 + 1
+    sl[2] = -5
+    bt[3, 1] = wl.num_blocks
+    bt[4, 2] = -1
+    bad, good = [1, 2, 3, 4], [0, 5, 6, 11, 17]
+    wl2 = W.Workload(**{**wl.__dict__, "block_tables": bt, "seq_lens": sl})
+    out, _ = gpu_decode(wl2, partition_size=ps)
+    g = out.double().numpy()
+    for s in bad:
+        assert np.isnan(g[s]).all(), s
+    assert_parity(g[good], oracle_decode(wl, seqs=good), "bf16", "rows beside the out-of-contract ones")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_permutation_bit_identical(dtype):
     wl = W.make_random(77, 6, 8, 2, 128, dtype, [1, 17, 100, 513, 1000, 2048], pool_factor=2.0)
