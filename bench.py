@@ -15,7 +15,9 @@ inputs already resident in HBM.  Prints ONE JSON line:
   roofline     the decode launches: algorithmic KV bytes / their mean duration
                (one pair of HIP events around the K back-to-back steps on the
                launch stream), against 8000 GB/s HBM3E peak; the flushed
-               median gives ``frac_flushed_p50``
+               median gives ``frac_flushed_p50``; ``traffic`` is the HBM bytes
+               per step from committed counter runs on the same kernel
+               sources (``frac_traffic`` prices the step on them)
   cpu_baseline the float64 oracle on the host cores: a process pool over the
                batch's sequences (one BLAS thread per process), run before the
                GPU is touched; a one-core walk of the same batch beside it
@@ -703,6 +705,7 @@ def bench_decode(args):
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
         if fp8:
             kernel += "|fp8"
+    traffic = traffic_for(kernel, f"cfg{cfg}")            # measured HBM bytes per step, if taken on these sources
     out_host = out.cpu().double().numpy()
     err = None
     if refs:
@@ -743,7 +746,8 @@ def bench_decode(args):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "frac_flushed_p50": (round(roof_bytes / (dist["p50"] / 1e6) / 1e9 / HBM_PEAK_GBS, 4)
                                  if dist else None),
-            "traffic": traffic_for(kernel, f"cfg{cfg}"),
+            "traffic": traffic,
+            "frac_traffic": round(traffic / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4) if traffic else None,
             "kernel": kernel,
             "bytes_per_launch": roof_bytes,
             "bytes": "unique K/V rows (a shared block counts once)" if shared else "K/V rows of the valid tokens",
