@@ -846,14 +846,16 @@ __device__ inline u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Query tiles of one pa_prefill_lds_kernel workgroup, and per wave: 16
-// tiles per workgroup, TW per wave (2: 8 waves, two per SIMD; 4: 4 waves, one
-// per SIMD with the accumulators in AGPRs).
-constexpr int kPfTilesPerGroup = 16;
+// Query tiles of one pa_prefill_lds_kernel workgroup (TPG) and per wave (TW).
+// TW = 2 is built (two waves per SIMD); TW = 4 (one wave per SIMD, the
+// accumulators in AGPRs) measured slower.  TPG = 16 (8 waves) for many
+// tiles per (sequence, kv head), TPG = 8 (4 waves, two workgroups per CU)
+// when a (sequence, kv head) has at most 8 tiles, so fewer waves idle.
 constexpr int kPfTilesPerWave = 2;
+constexpr int kPfSmallGroupTiles = 8;
 
-// Grid: one workgroup of 16 / TW waves per (sequence, kv head, 16
-// consecutive query tiles); wave w owns tiles 16*grp + TW*w .. TW*w + TW - 1
+// Grid: one workgroup of TPG / TW waves per (sequence, kv head, TPG
+// consecutive query tiles); wave w owns tiles TPG*grp + TW*w .. TW*w + TW - 1
 // (16 (token, head) rows each, as in pa_prefill_kernel).  The workgroup
 // streams the sequence's blocks in stages of kPfStageBlocks, double-buffered
 // in LDS with one barrier per stage: the waves copy the next stage's K and V
@@ -864,15 +866,15 @@ constexpr int kPfTilesPerWave = 2;
 //   PV: one 16x16x32 MFMA per 16 output columns over the pair's 32 keys, and
 //       one more against a column of ones, which sums each row's weights as
 //       rounded for the PV step (the softmax denominator).
-// Each K/V byte is read from memory once per 16 tiles instead of once per
+// Each K/V byte is read from memory once per TPG tiles instead of once per
 // tile, and from LDS once per TW tiles.  Rows past the sequence end, blocks
 // past the workgroup's last block and out-of-pool block ids load as zeros
 // (the buffer range of the block is cut to its valid rows).  The linear
 // workgroup id is split so that all workgroups of one (sequence, kv head)
 // land on the same XCD (workgroups are dealt to the 8 XCDs round robin),
 // where its K/V stay in that XCD's L2.
-template <class E, class KV, int D, int G, bool NT, int TW>
-__global__ void __launch_bounds__(64 * kPfTilesPerGroup / TW)
+template <class E, class KV, int D, int G, bool NT, int TW, int TPG>
+__global__ void __launch_bounds__(64 * TPG / TW)
 __attribute__((amdgpu_waves_per_eu(TW == 4 ? 1 : 2, TW == 4 ? 1 : 8)))
 pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, const char* __restrict__ k_cache,
                       const char* __restrict__ v_cache, const int* __restrict__ block_tables,
@@ -882,7 +884,8 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
   constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe;
-  constexpr int WAVES = kPfTilesPerGroup / TW;
+  constexpr int WAVES = TPG / TW;
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves per workgroup");
   static_assert(TW == 2 || TW == 4, "two or four tiles per wave");
   constexpr int RP = pf_k_pitch<D>(), VP = pf_v_pitch<D>(), KB = pf_k_bytes<D>(), SB = pf_stage_bytes<D>();
   constexpr int KVB = KV::kBytes;                     // bytes per element in the pools
@@ -900,7 +903,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   if (pair >= num_seqs * num_kv_heads) return;
   const int s = pair / num_kv_heads, kvh = pair - s * num_kv_heads;
   const int q0 = query_start[s], n = query_start[s + 1] - q0, L = seq_lens[s];
-  const int wg_tok0 = grp * kPfTilesPerGroup * TPT;
+  const int wg_tok0 = grp * TPG * TPT;
   if (n <= 0 || wg_tok0 >= n) return;                // the whole workgroup: uniform
   const bool bad_len = n > L || (int64_t)L > (int64_t)max_blocks * BS;
 
@@ -932,7 +935,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   const int my_b_end = active ? my_last / BS + 1 : 0;
   const int my_p_end = (my_b_end + 1) / 2;            // block pairs this wave consumes
   const int my_p_open = ((my_first + 1) / BS) / 2;    // pairs before this one are visible to every row
-  const int wg_last = L - n + min(wg_tok0 + kPfTilesPerGroup * TPT, n) - 1;
+  const int wg_last = L - n + min(wg_tok0 + TPG * TPT, n) - 1;
   const int wg_b_end = bad_len ? 0 : wg_last / BS + 1;
   const int* bt_row = block_tables + (int64_t)s * max_blocks;
 

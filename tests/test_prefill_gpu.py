@@ -84,6 +84,33 @@ def test_many_tile_kernel_edges(dtype, D, Hq, Hkv, fp8):
     assert_parity(g, ref, dtype, f"many-tile {dtype} D={D} {Hq}/{Hkv} fp8={fp8}")
 
 
+# At most 8 query tiles per (sequence, kv head): the many-tile kernel runs
+# workgroups of 8 tiles (4 waves).  G = 8: 16 tokens fill them, G = 4: 32.
+SMALL_LENS = [8, 10, 46, 48, 65, 33, 64, 165, 40, 31, 129, 200]
+SMALL_NQ = {8: [5, 6, 9, 16, 16, 12, 7, 16, 3, 16, 11, 14], 4: [9, 12, 17, 32, 31, 24, 13, 32, 20, 16, 30, 28]}
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,fp8", [("bf16", 128, 16, 2, False), ("f16", 64, 16, 2, False),
+                                                ("bf16", 128, 32, 8, False), ("bf16", 128, 32, 8, True)])
+def test_small_group_kernel_edges(dtype, D, Hq, Hkv, fp8):
+    G = Hq // Hkv
+    nq = np.minimum(SMALL_NQ[G], SMALL_LENS).tolist()
+    assert 2 < max(nq) * G / 16 <= 8
+    seed = zlib.crc32(f"small-{dtype}-{D}-{Hq}-{Hkv}-{fp8}".encode()) % 10000
+    wl, starts, q = _case(seed, Hq, Hkv, D, dtype, SMALL_LENS, nq)
+    if fp8:
+        kc8, vc8 = W.with_fp8_pools(wl, seed)
+        ks, vs = 1.0 / 128, 1.0 / 96
+        g = _gpu(wl, starts, q, kc8, vc8, fp8=(ks, vs))
+        ref = oracle.paged_prefill_ref(W.raw_numpy(q), kc8.numpy(), vc8.numpy(), wl.block_tables, wl.seq_lens,
+                                       starts, wl.scale, dtype, kv_dtype="e4m3", k_scale=ks, v_scale=vs)
+    else:
+        g = _gpu(wl, starts, q)
+        ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                       wl.block_tables, wl.seq_lens, starts, wl.scale, dtype)
+    assert_parity(g, ref, dtype, f"8-tile groups {dtype} D={D} {Hq}/{Hkv} fp8={fp8}")
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8)])
 def test_prefill_fp8_pools(Hq, Hkv):
     wl, starts, q = _case(600 + Hq, Hq, Hkv, 128, "bf16")
