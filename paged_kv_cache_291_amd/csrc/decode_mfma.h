@@ -997,14 +997,14 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   };
 
   // A step covers blocks 2p, 2p+1 of a stage for all tiles (key0: position
-  // of block 2p's first key), in three parts: scores (QK and the row maxima),
-  // rescale (rare: one branch for both tiles) and weights_pv (exponentials
+  // of block 2p's first key), in three parts: scores (QK and the lane maxima),
+  // rescale (rare: one branch for all tiles) and weights_pv (exponentials
   // and PV).  Every row sees key 0, and the first pair is consumed before any
   // other, so m_ref is finite whenever weights are taken.
   // raw scores: lane l holds row l%16, keys key0 + 16*(i/4) + 4*(l/16) + i%4
   struct Scores {
     float z[TW][8];
-    float bm[TW];                                     // row maxima, scaled
+    float zl[TW];                                     // this lane's maximum (raw); its row's is over 4 lanes
     bool vis[TW][8];                                  // visible keys (masked steps)
   };
   struct KOps { u32x4 a[KS], b[KS]; };                // K operands of blocks 2p and 2p+1
@@ -1045,23 +1045,26 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
       r.vis[t][i] = !MASKED || key0 + 16 * (i >> 2) + 4 * g + (i & 3) <= row_last[t];
       if (MASKED && !r.vis[t][i]) r.z[t][i] = -INFINITY;
     }
-    const float zm =
+    r.zl[t] =
         max_nonan(max_nonan(max_nonan(r.z[t][0], r.z[t][1], inf), max_nonan(r.z[t][2], r.z[t][3], inf), inf),
                   max_nonan(max_nonan(r.z[t][4], r.z[t][5], inf), max_nonan(r.z[t][6], r.z[t][7], inf), inf), inf);
-    r.bm[t] = rows_max_nonan(zm, inf) * qk_scale;
   };
+  // A row's maximum beats its reference by the threshold iff one of its four
+  // lanes' maxima does, so the (rare) rescale decides on the lane maxima and
+  // only then reduces them across the row's lanes.
   auto rescale = [&](const Scores& r) {
     bool up[TW], any = false;
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-      up[t] = r.bm[t] > st[t].m_ref + kRescaleThreshold;
+      up[t] = r.zl[t] * qk_scale > st[t].m_ref + kRescaleThreshold;
       any = any || up[t];
     }
     if (__ballot(any)) {
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
         if (!__ballot(up[t])) continue;
-        const float m_new = fmaxf(st[t].m_ref, r.bm[t]);
+        const float bm = rows_max_nonan(r.zl[t], inf) * qk_scale;       // row maxima, scaled
+        const float m_new = fmaxf(st[t].m_ref, bm);
         const float alpha = __builtin_amdgcn_exp2f(st[t].m_ref - m_new);   // 0 on the first pair
         float ar[4];
 #pragma unroll
