@@ -1146,12 +1146,19 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
         u32x4 vb[VE];
         v_read(sbuf, p - p_lo, vb);
         k_read(sbuf, p + 1 - p_lo, x);
+        // the matrix-core groups run at raised wave priority, so while one
+        // wave of the SIMD issues them the other's vector work fills the
+        // gaps (chunked-prefill batch: 265.9 -> 259.8 us on one box)
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
           const u32x4 pa = weights(std::false_type{}, t, cur);
+          __builtin_amdgcn_s_setprio(1);
           qk(t, x, nxt);
+          __builtin_amdgcn_s_setprio(0);
           if (t > 0) maxima(std::false_type{}, t - 1, 0, nxt);
+          __builtin_amdgcn_s_setprio(1);
           pv(t, pa, vb);
+          __builtin_amdgcn_s_setprio(0);
         }
         maxima(std::false_type{}, TW - 1, 0, nxt);
         cur = nxt;
