@@ -824,13 +824,14 @@ pa_prefill_kernel(void* __restrict__ out, const void* __restrict__ query, const 
 
 // LDS stage of kPfStageBlocks blocks, K rows then V rows, 16-bit elements
 // whatever the pool type, each region row-major at a padded pitch:
-//  * K (pitch 2D + 16): the 16 lanes reading one QK operand (16 rows, same
-//    16 bytes) hit 16 different bank groups;
+//  * K (pitch 2D + 32): each lane reads 16 bytes of one of 16 rows for a QK
+//    operand; the counters show no bank conflicts at this pitch (at 2D + 16:
+//    0.40 conflict cycles per LDS access, the LDS busy 34 % instead of 24 %);
 //  * V (pitch 2D + 32): the PV operands come from transposing reads, where 8
 //    rows x 32 bytes are read together; a 32-byte shift per row keeps those
 //    in different banks.
 constexpr int kPfStageBlocks = 4;
-template <int D> constexpr int pf_k_pitch() { return D * 2 + 16; }
+template <int D> constexpr int pf_k_pitch() { return D * 2 + 32; }
 template <int D> constexpr int pf_v_pitch() { return D * 2 + 32; }
 template <int D> constexpr int pf_k_bytes() { return kPfStageBlocks * kBlockSize * pf_k_pitch<D>(); }
 template <int D> constexpr int pf_stage_bytes() { return kPfStageBlocks * kBlockSize * (pf_k_pitch<D>() + pf_v_pitch<D>()); }
