@@ -694,17 +694,17 @@ def bench_decode(args):
     ms_per_step = wall * 1e3 / K
     value = kv / (wall / K) / 1e9
     achieved = roof_bytes / (mean_ms / 1e3) / 1e9
-    # the launch the library picks: the vector-ALU core for fp32, and for
-    # 16-bit pools with one query head per kv head (with partitions, or from
-    # 1024 (sequence, kv head) pairs)
-    valu = wl.dtype == "f32" or (not fp8 and wl.num_heads == wl.num_kv_heads
-                                 and (ps > 0 or wl.num_seqs * wl.num_kv_heads >= 1024))
+    # the launch the library picks: the vector-ALU core for fp32, and with one
+    # query head per kv head for 16-bit pools (with partitions, or from 1024
+    # (sequence, kv head) pairs) and for fp8 pools with partitions
+    valu = wl.dtype == "f32" or (wl.num_heads == wl.num_kv_heads
+                                 and (ps > 0 or (not fp8 and wl.num_seqs * wl.num_kv_heads >= 1024)))
     if valu:
         kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 else "")
     else:
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
-        if fp8:
-            kernel += "|fp8"
+    if fp8:
+        kernel += "|fp8"
     traffic = traffic_for(kernel, f"cfg{cfg}")            # measured HBM bytes per step, if taken on these sources
     out_host = out.cpu().double().numpy()
     err = None

@@ -162,11 +162,15 @@ __device__ inline void store_run(void* base, int64_t elem, const float* f) {
 #pragma unroll
     for (int e = 0; e < N; e += 4)
       *reinterpret_cast<float4*>(static_cast<float*>(base) + elem + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
-  } else if constexpr (N == 8) {
-    const u32x4 w = {pack2<E>(f[0], f[1]), pack2<E>(f[2], f[3]), pack2<E>(f[4], f[5]), pack2<E>(f[6], f[7])};
-    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + elem) = w;
+  } else if constexpr (N % 8 == 0) {
+#pragma unroll
+    for (int e = 0; e < N; e += 8) {
+      const u32x4 w = {pack2<E>(f[e], f[e + 1]), pack2<E>(f[e + 2], f[e + 3]), pack2<E>(f[e + 4], f[e + 5]),
+                       pack2<E>(f[e + 6], f[e + 7])};
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + elem + e) = w;
+    }
   } else {
-    static_assert(N == 4, "16-bit runs are 4 or 8 elements");
+    static_assert(N == 4, "16-bit runs are 4 or a multiple of 8 elements");
     const u32x2 w = {pack2<E>(f[0], f[1]), pack2<E>(f[2], f[3])};
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + elem) = w;
   }
@@ -204,6 +208,13 @@ template <bool NT>
 __device__ inline uint32_t load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, NT ? 2 : 0);
 }
+
+// Formats of the K/V pools.  Kv16: elements of the query type (bf16 or
+// fp16).  KvFp8: OCP fp8 e4m3 codes, dequantised in registers to the query
+// type (exactly: every e4m3 value is a bf16 and an fp16 value); the pools'
+// scales enter the score scale (K) and the final normalisation (V).
+struct Kv16 { static constexpr int kBytes = 2; };   // (fp32 queries: fp32 pools)
+struct KvFp8 { static constexpr int kBytes = 1; };
 
 // Two OCP fp8 e4m3 values (bytes 0-1, or 2-3 when `hi`) of a dword as two
 // 16-bit values of type E in one dword.  Every e4m3 value is exact in bf16

@@ -61,13 +61,6 @@ struct MfmaState {
   f32x4 acc[MfmaShape<D>::kVe];   // O[h = 4*(l/16) + i][d = VE*(l%16) + T]
 };
 
-// Formats of the K/V pools.  Kv16: elements of the query type (bf16 or
-// fp16).  KvFp8: OCP fp8 e4m3 codes, dequantised in registers to the query
-// type (exactly: every e4m3 value is a bf16 and an fp16 value); the pools'
-// scales enter the score scale (K) and the final normalisation (V).
-struct Kv16 { static constexpr int kBytes = 2; };
-struct KvFp8 { static constexpr int kBytes = 1; };
-
 // Where each lane's K/V bytes are and how they become MFMA operands.  For a
 // QK step the lane (c = l%16, g = l/16) supplies 8 consecutive elements of K
 // row c; which 8 (the map d(g, step)) only has to agree with the query

@@ -1,5 +1,5 @@
-// Paged decode on the vector ALUs (fp32 KV, and 16-bit KV with one query
-// head per kv head, where a matrix-core tile would be 1/16 dense).
+// Paged decode on the vector ALUs (fp32 KV, and 16-bit or fp8 KV with one
+// query head per kv head, where a matrix-core tile would be 1/16 dense).
 //
 // One 64-lane wave (one workgroup) per work item (sequence, kv head, chunk of
 // tokens; with part_tokens == 0 the chunk is the whole sequence):
@@ -19,19 +19,27 @@
 //    can weight its V slice; PV accumulates in fp32 registers.
 //  * At the end the sub-waves are merged with log-sum-exp weights.
 //  * Masking uses selects only (the pool may hold NaN in dead slots).
+//  * fp8 (e4m3) pools: a 16-byte load holds 16 codes of a row; K codes are
+//    widened in pairs to the query type for the dot products, V codes to
+//    fp32; the pool scales enter the score scale (K) and the final
+//    normalisation (V).
 #pragma once
 
 #include "common.h"
 
 namespace pa {
 
-template <class E, int D, int G>
+template <class E, class KV, int D, int G>
 struct ValuCfg {
-  static constexpr int kRow = D * E::kBytes;        // bytes of one token row of one head
+  static constexpr bool kFp8 = std::is_same<KV, KvFp8>::value;
+  static constexpr int kKvBytes = kFp8 ? 1 : E::kBytes;   // bytes per pool element
+  static constexpr int kRow = D * kKvBytes;         // bytes of one token row of one head in the pools
+  static constexpr int kQRow = D * E::kBytes;       // ... of the query
   static constexpr int kLpr = kRow / 16;            // lanes per row
   static constexpr int kRpi = 64 / kLpr;            // rows per load instruction
   static constexpr int kNi = kBlockSize / kRpi;     // load instructions per block
-  static constexpr int kEpl = 16 / E::kBytes;       // elements per lane per instruction
+  static constexpr int kEpl = 16 / kKvBytes;        // elements per lane per instruction
+  static constexpr int kQw = kEpl * E::kBytes / 16; // 16-byte query chunks per lane and head
   static constexpr int kNv = kNi * G;               // partial scores per lane per block
   static constexpr int kNvl = kNv > kLpr ? kNv / kLpr : 1;
   static constexpr int kNh = ilog2(kNv < kLpr ? kNv : kLpr);
@@ -47,17 +55,55 @@ struct ValuOccupancy {
   static constexpr int kWaves = (G <= 4 && (E::kBytes == 2 || D == 64)) ? 3 : 1;
 };
 
+// Dot product of a lane's query chunks with one 16-byte chunk of a K row.
+template <class E, class KV>
+__device__ inline float dot_chunk(const u32x4* q, const u32x4& k) {
+  if constexpr (std::is_same<KV, KvFp8>::value) {
+    // 16 codes; code pair (2j, 2j+1) against query dword j
+    const uint32_t qw[8] = {q[0][0], q[0][1], q[0][2], q[0][3], q[1][0], q[1][1], q[1][2], q[1][3]};
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 kk = {fp8x2_to<E, false>(k[j]), fp8x2_to<E, true>(k[j]), 0u, 0u};
+      acc = dot16<E>(u32x4{qw[2 * j], qw[2 * j + 1], 0u, 0u}, kk, acc);
+    }
+    return acc;
+  } else {
+    return dot16<E>(q[0], k, 0.f);
+  }
+}
+
+// One 16-byte chunk of a V row as fp32.
+template <class E, class KV>
+__device__ inline void widen_chunk(const u32x4& v, float* f) {
+  if constexpr (std::is_same<KV, KvFp8>::value) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)v[j], 1.0f, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)v[j], 1.0f, true);
+      f[4 * j] = lo.x;
+      f[4 * j + 1] = lo.y;
+      f[4 * j + 2] = hi.x;
+      f[4 * j + 3] = hi.y;
+    }
+  } else {
+    widen16<E>(v, f);
+  }
+}
+
 // ws: partial records [num_seqs * num_heads * num_parts] (split mode only).
 // NT: K/V loads with the non-temporal policy (blocks read once per call).
-template <class E, int D, int G, bool NT>
+// v_scale multiplies the output (the V pool's scale; 1 for 16-bit pools).
+template <class E, class KV, int D, int G, bool NT>
 __global__ void __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(ValuOccupancy<E, D, G>::kWaves, 8)))
 pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
                       const char* __restrict__ k_cache, const char* __restrict__ v_cache,
                       const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                       int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
-                      float qk_scale, int part_tokens, int num_parts, float* __restrict__ ws) {
-  using C = ValuCfg<E, D, G>;
+                      float qk_scale, float v_scale, int part_tokens, int num_parts, float* __restrict__ ws) {
+  using C = ValuCfg<E, KV, D, G>;
   constexpr int BS = kBlockSize;
   constexpr int LPR = C::kLpr, RPI = C::kRpi, NI = C::kNi, EPL = C::kEpl;
   constexpr int NV = C::kNv, NVL = C::kNvl, NH = C::kNh;
@@ -78,11 +124,14 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
   const int s = w / num_parts;
   const int hq0 = kvh * G;                                      // first query head of the group
 
-  u32x4 qv[G];
+  u32x4 qv[G][C::kQw];                                          // query elements c*EPL .. c*EPL+EPL-1
   {
-    const char* qb = static_cast<const char*>(query) + ((int64_t)s * num_heads + hq0) * C::kRow + c * 16;
+    const char* qb = static_cast<const char*>(query) + ((int64_t)s * num_heads + hq0) * C::kQRow +
+                     c * EPL * E::kBytes;
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const u32x4*>(qb + h * C::kRow);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int w = 0; w < C::kQw; ++w) qv[h][w] = *reinterpret_cast<const u32x4*>(qb + h * C::kQRow + 16 * w);
   }
 
   const int L = seq_lens[s];
@@ -131,7 +180,7 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) sc[i * G + h] = dot16<E>(qv[h], kb[i], 0.f);
+      for (int h = 0; h < G; ++h) sc[i * G + h] = dot_chunk<E, KV>(qv[h], kb[i]);
     transpose_reduce<LPR, NV, ilog2(LPR) - 1>(sc, c);
 
     float p[NVL], alpha[NVL];
@@ -172,7 +221,7 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
       u32x4 v = vb[i];
       if (masked && i * RPI + r >= valid) v = u32x4{0u, 0u, 0u, 0u};
       float vf[EPL];
-      widen16<E>(v, vf);
+      widen_chunk<E, KV>(v, vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float ph = pall[i * G + h];
@@ -247,7 +296,7 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
   if (r != 0) return;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float inv = Lh[h] > 0.f ? 1.f / Lh[h] : 0.f;
+    const float inv = Lh[h] > 0.f ? v_scale / Lh[h] : 0.f;
     float o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = bad ? qnan() : acc[h][e] * inv;

@@ -238,15 +238,15 @@ int launch_mfma(const Args& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-template <class E, int D, int G>
+template <class E, class KV, int D, int G>
 int launch_valu(const Args& a, hipStream_t st) {
   const long long grid = (long long)a.num_seqs * a.num_parts * a.num_kv_heads;
   if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   float* ws = static_cast<float*>(a.ws);
-  auto k = a.stream_kv ? pa_decode_valu_kernel<E, D, G, true> : pa_decode_valu_kernel<E, D, G, false>;
+  auto k = a.stream_kv ? pa_decode_valu_kernel<E, KV, D, G, true> : pa_decode_valu_kernel<E, KV, D, G, false>;
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64), 0, st,
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                     a.num_blocks, a.qk_scale, a.part_tokens, a.num_parts, ws);
+                     a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, ws);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (a.part_tokens > 0) {
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
@@ -268,13 +268,21 @@ constexpr long long kValuMhaMinItems = 1024;
 template <class E, int D, int G>
 int launch(const Args& a, hipStream_t st) {
   if constexpr (E::kBytes == 4) {
-    return launch_valu<E, D, G>(a, st);
+    return launch_valu<E, Kv16, D, G>(a, st);
   } else if (a.fp8_kv) {
+    // fp8 pools without grouping: the vector-ALU core only with partitions
+    // (13B-shaped batch, 512-token partitions: 163.0 against 184.9 us for the
+    // matrix-core split); without them the balanced split on the matrix cores
+    // is faster (150.4 against 168.3 us: a wave's 2 KiB per block is too
+    // little in flight, and its rows are 128-byte pieces at a 5 KiB stride)
+    if constexpr (G == 1) {
+      if (a.part_tokens > 0) return launch_valu<E, KvFp8, D, G>(a, st);
+    }
     return a.stream_kv ? launch_mfma<E, KvFp8, D, G, true>(a, st) : launch_mfma<E, KvFp8, D, G, false>(a, st);
   } else {
     if constexpr (G == 1) {
       if (a.part_tokens > 0 || (long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems)
-        return launch_valu<E, D, G>(a, st);
+        return launch_valu<E, Kv16, D, G>(a, st);
     }
     return a.stream_kv ? launch_mfma<E, Kv16, D, G, true>(a, st) : launch_mfma<E, Kv16, D, G, false>(a, st);
   }

@@ -96,6 +96,18 @@ def test_fp8_decode_8b_batch_full_size():
         assert_parity(g, ref, "bf16", f"fp8 8B batch ps={ps}, every sequence")
 
 
+def test_fp8_decode_13b_batch_full_size():
+    """64 sequences x 40 heads without grouping: every row, on the balanced
+    split (matrix cores) and with 512-token partitions (the vector-ALU core
+    reading the fp8 codes)."""
+    wl = W.make_config(2, 0, poison=True)
+    kc8, vc8 = _fp8_case(wl, 34)
+    ref = _ref_fp8(wl, kc8, vc8)
+    for ps in (0, 512):
+        g = _run_fp8(wl, kc8, vc8, ps)
+        assert_parity(g, ref, wl.dtype, f"fp8 13B batch ps={ps}, every sequence")
+
+
 def test_fp8_copy_blocks_bit_exact():
     NB, BS, Hkv, D = 200, 16, 8, 128
     kc = W.random_fp8_codes(5, (NB, BS, Hkv, D))

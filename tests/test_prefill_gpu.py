@@ -136,9 +136,12 @@ def test_prefill_non_positive_scale(scale, lens, nq):
     assert_parity(g, ref, "bf16", f"prefill scale {scale} max_q={max(nq)}")
 
 
-def test_prefill_contract_violations_give_nan_rows():
-    lens, nq = [40, 20, 30, 50], [3, 4, 2, 5]
-    wl, starts, q = _case(71, 8, 2, 64, "bf16", lens, nq)
+@pytest.mark.parametrize("D,nq", [(64, [3, 4, 2, 5]), (128, [3, 4, 2, 12])])
+def test_prefill_contract_violations_give_nan_rows(D, nq):
+    """Out-of-contract sequences give NaN rows; 12 query tokens of 4 heads per
+    kv head take the many-tile kernel."""
+    lens = [40, 20, 30, 50]
+    wl, starts, q = _case(71, 8, 2, D, "bf16", lens, nq)
     bt, sl = wl.block_tables.copy(), wl.seq_lens.copy()
     sl[1] = 3                                             # fewer tokens than query rows
     sl[2] = bt.shape[1] * 16 + 1                          # past the table row
