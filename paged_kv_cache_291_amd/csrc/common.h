@@ -58,6 +58,15 @@ __device__ inline uint16_t bf16_bits(float x) {
 // acc + <q slice, k slice> over one 16-byte chunk.
 // Elements are copied out of the vectors before __builtin_bit_cast: applied
 // directly to a vector-subscript lvalue, the cast reads element 0.
+// acc + q.lo*k.lo + q.hi*k.hi over two 16-bit elements per dword (fp32 sum).
+template <class E>
+__device__ inline float dot2(uint32_t q, uint32_t k, float acc) {
+  if constexpr (std::is_same<E, ElemBF16>::value)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q), __builtin_bit_cast(bf16x2_t, k), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q), __builtin_bit_cast(f16x2_t, k), acc, false);
+}
+
 template <class E>
 __device__ inline float dot16(const u32x4& q, const u32x4& k, float acc);
 

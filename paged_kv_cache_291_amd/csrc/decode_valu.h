@@ -64,8 +64,8 @@ __device__ inline float dot_chunk(const u32x4* q, const u32x4& k) {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 kk = {fp8x2_to<E, false>(k[j]), fp8x2_to<E, true>(k[j]), 0u, 0u};
-      acc = dot16<E>(u32x4{qw[2 * j], qw[2 * j + 1], 0u, 0u}, kk, acc);
+      acc = dot2<E>(qw[2 * j], fp8x2_to<E, false>(k[j]), acc);
+      acc = dot2<E>(qw[2 * j + 1], fp8x2_to<E, true>(k[j]), acc);
     }
     return acc;
   } else {
