@@ -925,6 +925,13 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   }
   const u32x4 ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
   const float inf = opaque_inf();
+  // a tile rescales when a lane maximum (raw) exceeds thr = (m_ref + 8) / scale
+  // (the threshold is a heuristic: rounding here changes nothing but when
+  // the exact re-association happens); updated with m_ref
+  const float inv_scale = 1.f / qk_scale;
+  float thr[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) thr[t] = -INFINITY;
   const int my_first = L - n + tok0, my_last = L - n + min(tok0 + TW * TPT, n) - 1;
   const int my_b_end = active ? my_last / BS + 1 : 0;
   const int my_p_end = (my_b_end + 1) / 2;            // block pairs this wave consumes
@@ -1050,7 +1057,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
     bool up[TW], any = false;
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-      up[t] = r.zl[t] * qk_scale > st[t].m_ref + kRescaleThreshold;
+      up[t] = r.zl[t] > thr[t];
       any = any || up[t];
     }
     if (__ballot(any)) {
@@ -1070,6 +1077,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc_l[t][i] *= ar[i];
         st[t].m_ref = m_new;
+        thr[t] = (m_new + kRescaleThreshold) * inv_scale;
       }
     }
   };
