@@ -51,8 +51,9 @@ struct ValuCfg {
 
 template <class E, int D, int G>
 struct ValuOccupancy {
-  // 3 waves per SIMD need <= 168 VGPRs, which head_size 64 meets up to G = 4
-  static constexpr int kWaves = (G <= 4 && (E::kBytes == 2 || D == 64)) ? 3 : 1;
+  // 3 waves per SIMD need <= 168 VGPRs, which head_size 64 meets up to G = 4;
+  // 128-wide 16-bit rows hold three blocks of K and V in registers, 2 waves
+  static constexpr int kWaves = (G <= 4 && D == 64) ? 3 : (G <= 4 && E::kBytes == 2) ? 2 : 1;
 };
 
 // Dot product of a lane's query chunks with one 16-byte chunk of a K row.
@@ -237,28 +238,44 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
     const int n = min(64, b_end - cb);
     const int id = lane < n ? bt[cb + lane] : 0;
     if (__ballot(lane < n && (unsigned)id >= (unsigned)num_blocks)) { bad = true; break; }
-    const bool last_batch = cb + 64 >= b_end;
-    const int last_valid = t_end - (b_end - 1) * BS;
-    u32x4 ka[NI], va[NI], kb2[NI], vb2[NI];
-    load_block(__builtin_amdgcn_readlane(id, 0), ka, va);
+    // valid rows of the batch's last block (only the sequence's last block is partial)
+    const int v_last = cb + 64 >= b_end ? t_end - (b_end - 1) * BS : BS;
+    auto blk = [&](int j) { return __builtin_amdgcn_readlane(id, j); };
+    auto consume_last = [&](const u32x4* kb, const u32x4* vb) {
+      if (v_last >= BS) consume(kb, vb, BS, false);
+      else consume(kb, vb, v_last, true);
+    };
+    // three register sets: two blocks in flight while one is consumed
+    u32x4 ka[NI], va[NI], kb2[NI], vb2[NI], kc[NI], vc[NI];
+    load_block(blk(0), ka, va);
+    if (n > 1) load_block(blk(1), kb2, vb2);
     int j = 0;
-    for (; j + 2 < n; j += 2) {                                 // blocks j, j+1 full; j+2 exists
-      load_block(__builtin_amdgcn_readlane(id, j + 1), kb2, vb2);
+    for (; j + 4 < n; j += 3) {                                 // blocks j..j+2 full; j+3, j+4 exist
+      load_block(blk(j + 2), kc, vc);
       consume(ka, va, BS, false);
-      load_block(__builtin_amdgcn_readlane(id, j + 2), ka, va);
+      load_block(blk(j + 3), ka, va);
       consume(kb2, vb2, BS, false);
+      load_block(blk(j + 4), kb2, vb2);
+      consume(kc, vc, BS, false);
     }
-    const int vj = (last_batch && j == n - 1) ? last_valid : BS;
-    if (j + 1 < n) {
-      load_block(__builtin_amdgcn_readlane(id, j + 1), kb2, vb2);
+    // 1..4 blocks left: j in ka/va, j + 1 (if any) in kb2/vb2
+    const int rem = n - j;
+    if (rem == 1) {
+      consume_last(ka, va);
+    } else if (rem == 2) {
       consume(ka, va, BS, false);
-      const int vj1 = last_batch ? last_valid : BS;
-      if (vj1 >= BS) consume(kb2, vb2, BS, false);
-      else consume(kb2, vb2, vj1, true);
-    } else if (vj >= BS) {
-      consume(ka, va, BS, false);
+      consume_last(kb2, vb2);
     } else {
-      consume(ka, va, vj, true);
+      load_block(blk(j + 2), kc, vc);
+      consume(ka, va, BS, false);
+      if (rem == 4) load_block(blk(j + 3), ka, va);
+      consume(kb2, vb2, BS, false);
+      if (rem == 3) {
+        consume_last(kc, vc);
+      } else {
+        consume(kc, vc, BS, false);
+        consume_last(ka, va);
+      }
     }
   }
 
