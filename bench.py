@@ -695,12 +695,11 @@ def bench_decode(args):
     value = kv / (wall / K) / 1e9
     achieved = roof_bytes / (mean_ms / 1e3) / 1e9
     # the launch the library picks: the vector-ALU core for fp32, and with one
-    # query head per kv head for 16-bit pools (with partitions, or from 1024
-    # (sequence, kv head) pairs) and for fp8 pools with partitions
-    valu = wl.dtype == "f32" or (wl.num_heads == wl.num_kv_heads
-                                 and (ps > 0 or (not fp8 and wl.num_seqs * wl.num_kv_heads >= 1024)))
-    if valu:
-        kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 else "")
+    # query head per kv head (with partitions, or from 1024 (sequence, kv
+    # head) pairs; over fp8 pools then cut into partitions by the library)
+    mha = wl.num_heads == wl.num_kv_heads and (ps > 0 or wl.num_seqs * wl.num_kv_heads >= 1024)
+    if wl.dtype == "f32" or mha:
+        kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 or (fp8 and mha) else "")
     else:
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
     if fp8:

@@ -76,8 +76,9 @@ const char* pa_status_string(int status);
 /*
  * Bytes of device workspace paged_attention_decode needs (an upper bound):
  *  partition_size > 0:
- *    num_seqs * num_heads * ceil(max_seq_len / partition_size) * (head_size + 4) * 4
- *    (one fp32 partial record per partition: max, sum, 2 unused, output)
+ *    256 + num_seqs * num_heads * ceil(max_seq_len / partition_size) * (head_size + 4) * 4
+ *    (a 256-byte header holding a work-queue counter, then one fp32 partial
+ *    record per partition: max, sum, 2 unused, output)
  *  partition_size == 0 (balanced split, bf16/fp16 KV):
  *    round_up(num_seqs * 16, 256) + 256 * num_heads * 2 * (head_size + 4) * 4
  *    (one 16-byte entry per sequence saying where its partial results are,
@@ -121,7 +122,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  *                 fp32 one pass per (sequence, kv head), no workspace; so
  *                 too for bf16/fp16 with num_heads == num_kv_heads and at
  *                 least 1024 (sequence, kv head) pairs (the workspace is
- *                 still required).
+ *                 still required).  Over fp8 pools (paged_attention_decode_fp8)
+ *                 with num_heads == num_kv_heads and at least 1024 pairs the
+ *                 library picks a partition size (512 tokens, or more where
+ *                 the records would not fit this workspace) and runs the
+ *                 split below; lengths above max_seq_len then give NaN rows.
  *                 > 0: split context into partitions of this many tokens (a
  *                 multiple of block_size); a second kernel merges partitions
  *                 with log-sum-exp weights.  Needs a workspace.

@@ -141,8 +141,19 @@ int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ?
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Fixed split: a 256-byte header (the work-queue counter of the vector-ALU
+// launch), then one partial record per (sequence, query head, partition).
+constexpr size_t kQueueHeaderBytes = 256;
 size_t split_workspace_bytes(int num_seqs, int num_heads, int head_size, int num_parts) {
-  return (size_t)num_seqs * num_heads * num_parts * (head_size + kRecHead) * sizeof(float);
+  return kQueueHeaderBytes + (size_t)num_seqs * num_heads * num_parts * (head_size + kRecHead) * sizeof(float);
+}
+
+// Partitions per sequence of the fixed split: max_seq_len, or the table
+// row's capacity when 0 is passed, in partition_size pieces.
+int split_num_parts(int block_size, int max_blocks_per_seq, int max_seq_len, int partition_size) {
+  const long long cap = (long long)max_blocks_per_seq * block_size;
+  const int msl = max_seq_len > 0 ? max_seq_len : (int)(cap < 0x7fffffffLL ? cap : 0x7fffffffLL);
+  return msl > 0 ? ceil_div(msl, partition_size) : 1;
 }
 
 // Balanced split: one 16-byte entry per sequence (where its records are),
@@ -188,12 +199,38 @@ int mq_tiles(int num_heads, int num_kv_heads, int max_q) {      // kSkMaxTiles +
 struct Args {
   void* out; const void* query; const char* kc; const char* vc;
   const int* bt; const int* sl;
-  int num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks;
+  int num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks, max_seq_len;
   float qk_scale, v_scale;
   int part_tokens, num_parts;
   void* ws;
   bool stream_kv, fp8_kv;
+  bool queue;   // vector-ALU launch with partitions: workgroups take items from a counter
 };
+
+// Sets the vector-ALU launch's work-queue counter to 0 (a kernel rather than a
+// memset, so that the call can be captured in a graph).
+__global__ void __launch_bounds__(64) pa_queue_reset_kernel(int* __restrict__ queue) {
+  if (threadIdx.x == 0) queue[0] = 0;
+}
+
+// Workgroups of `kernel` (`threads` lanes, no dynamic LDS) the current device
+// holds at once; found once per device and kernel (one workgroup size per
+// kernel), 0 if the runtime cannot tell.
+template <class K>
+int resident_workgroups(K kernel, int threads) {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  n = cus * per_cu;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 template <class E, class KV, int D, int G, bool NT>
 int launch_mfma(const Args& a, hipStream_t st) {
@@ -210,7 +247,7 @@ int launch_mfma(const Args& a, hipStream_t st) {
     // half-empty last round whenever the rounds are odd in number).
     const long long wgs = kSkWorkgroups >= groups ? kSkWorkgroups / groups * groups : groups;
     const long long grid = items <= 2 * wgs ? (items < wgs ? items : wgs) : items;
-    float* ws = static_cast<float*>(a.ws);
+    float* ws = reinterpret_cast<float*>(static_cast<char*>(a.ws) + kQueueHeaderBytes);
     hipLaunchKernelGGL((pa_decode_mfma_kernel<E, KV, D, G, NT>), dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                        a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
                        a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, hpw, (int)items, ws);
@@ -238,15 +275,32 @@ int launch_mfma(const Args& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+// One single-wave workgroup per (sequence, kv head[, partition]); or, with
+// partitions and a.queue, workgroups of up to kValuMaxHeadsPerWg kv heads, as
+// many as the GPU holds at once, that take (sequence, partition, head group)
+// items from a counter in the workspace header.
 template <class E, class KV, int D, int G>
 int launch_valu(const Args& a, hipStream_t st) {
-  const long long grid = (long long)a.num_seqs * a.num_parts * a.num_kv_heads;
-  if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-  float* ws = static_cast<float*>(a.ws);
+  const bool queued = a.queue && a.part_tokens > 0;
+  const int hpw = queued ? heads_per_workgroup(a.num_kv_heads, kValuMaxHeadsPerWg) : 1;
+  const long long items = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
+  if (items > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
   auto k = a.stream_kv ? pa_decode_valu_kernel<E, KV, D, G, true> : pa_decode_valu_kernel<E, KV, D, G, false>;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64), 0, st,
+  long long grid = items;
+  int* queue = nullptr;
+  float* ws = nullptr;
+  if (a.part_tokens > 0) ws = reinterpret_cast<float*>(static_cast<char*>(a.ws) + kQueueHeaderBytes);
+  if (queued) {
+    queue = static_cast<int*>(a.ws);
+    int slots = resident_workgroups(k, 64 * hpw);
+    if (slots <= 0) slots = kSkWorkgroups * 4 * ValuOccupancy<E, KV, D, G>::kWaves / hpw;
+    grid = items < slots ? items : slots;
+    hipLaunchKernelGGL(pa_queue_reset_kernel, dim3(1), dim3(64), 0, st, queue);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                     a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, ws);
+                     a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, ws, (int)items, queue);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (a.part_tokens > 0) {
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
@@ -257,26 +311,43 @@ int launch_valu(const Args& a, hipStream_t st) {
 }
 
 // One query head per kv head (no grouping) leaves the matrix-core tile 1/16
-// dense; there 16-bit pools take the vector-ALU core, one wave per (sequence,
-// kv head[, partition]) (13B-shaped batch, 64 seqs x 40 heads: 254.9 us
-// against 257.1 us for the balanced split on the matrix cores; with 512-token
-// partitions 257.7 against 319.3 us).  Without partitions that needs enough
+// dense; there the vector-ALU core runs.  Over 16-bit pools one workgroup per
+// (sequence, kv head[, partition]) (13B-shaped batch, 64 seqs x 40 heads:
+// 250.6 us; fed from the work queue with 512-token partitions 262 us).  Over
+// fp8 pools, where a wave's share of a block is half as large, the work queue
+// with partitions wins: 144.9 us (512-token partitions chosen here) and 145.3
+// us (partition_size 512), against 150.4 us for the balanced split on the
+// matrix cores and 157.2 us for one workgroup per item.  Both need enough
 // (sequence, kv head) items to keep every CU busy; fewer take the balanced
-// split.
+// split on the matrix cores.
 constexpr long long kValuMhaMinItems = 1024;
+constexpr int kValuPartTokens = 512;
+
+// Partition size of the queue-fed vector-ALU launch for partition_size 0
+// (0: the records would not fit at any size; the caller takes another path).
+int valu_part_tokens(const Args& a, int head_size) {
+  const size_t cap = balanced_workspace_bytes(a.num_seqs, a.num_heads, head_size);
+  for (int pt = kValuPartTokens; pt <= (1 << 29); pt *= 2) {
+    const int np = split_num_parts(kBlockSize, a.max_blocks, a.max_seq_len, pt);
+    if (np <= 1 || split_workspace_bytes(a.num_seqs, a.num_heads, head_size, np) <= cap) return pt;
+  }
+  return 0;
+}
 
 template <class E, int D, int G>
 int launch(const Args& a, hipStream_t st) {
   if constexpr (E::kBytes == 4) {
     return launch_valu<E, Kv16, D, G>(a, st);
   } else if (a.fp8_kv) {
-    // fp8 pools without grouping: the vector-ALU core only with partitions
-    // (13B-shaped batch, 512-token partitions: 163.0 against 184.9 us for the
-    // matrix-core split); without them the balanced split on the matrix cores
-    // is faster (150.4 against 168.3 us: a wave's 2 KiB per block is too
-    // little in flight, and its rows are 128-byte pieces at a 5 KiB stride)
     if constexpr (G == 1) {
-      if (a.part_tokens > 0) return launch_valu<E, KvFp8, D, G>(a, st);
+      Args b = a;
+      b.queue = true;
+      if (a.part_tokens > 0) return launch_valu<E, KvFp8, D, G>(b, st);
+      b.part_tokens = (long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems ? valu_part_tokens(a, D) : 0;
+      if (b.part_tokens > 0) {
+        b.num_parts = split_num_parts(kBlockSize, a.max_blocks, a.max_seq_len, b.part_tokens);
+        return launch_valu<E, KvFp8, D, G>(b, st);
+      }
     }
     return a.stream_kv ? launch_mfma<E, KvFp8, D, G, true>(a, st) : launch_mfma<E, KvFp8, D, G, false>(a, st);
   } else {
@@ -370,13 +441,6 @@ int scratch_address(void* stream, void** ptr) {
   return PA_OK;
 }
 
-// Partitions per sequence of the fixed split: max_seq_len, or the table
-// row's capacity when 0 is passed, in partition_size pieces.
-int split_num_parts(int block_size, int max_blocks_per_seq, int max_seq_len, int partition_size) {
-  const long long cap = (long long)max_blocks_per_seq * block_size;
-  const int msl = max_seq_len > 0 ? max_seq_len : (int)(cap < 0x7fffffffLL ? cap : 0x7fffffffLL);
-  return msl > 0 ? ceil_div(msl, partition_size) : 1;
-}
 
 // Workspace bytes a decode call with these (already validated) sizes uses.
 size_t decode_workspace_need(int num_seqs, int num_heads, int head_size, int block_size, int max_blocks_per_seq,
@@ -426,7 +490,7 @@ int decode_impl(void* out, const void* query, const void* k_cache, const void* v
   a.kc = static_cast<const char*>(k_cache); a.vc = static_cast<const char*>(v_cache);
   a.bt = block_tables; a.sl = seq_lens;
   a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
-  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.max_seq_len = max_seq_len;
   a.qk_scale = (float)((double)scale * (double)k_scale * 1.4426950408889634);
   a.v_scale = v_scale;
   a.fp8_kv = fp8_kv;

@@ -42,9 +42,9 @@ def test_status_strings():
 
 
 def test_workspace_size_formula():
-    # fixed partitions: one record of head_size + 4 floats per (sequence, head, partition)
-    assert P.pa_decode_workspace_size(8, 64, 128, 32768, 512) == 8 * 64 * 64 * 132 * 4
-    assert P.pa_decode_workspace_size(3, 5, 64, 100, 16) == 3 * 5 * 7 * 68 * 4
+    # fixed partitions: a 256-byte queue header + one record of head_size + 4 floats per (sequence, head, partition)
+    assert P.pa_decode_workspace_size(8, 64, 128, 32768, 512) == 256 + 8 * 64 * 64 * 132 * 4
+    assert P.pa_decode_workspace_size(3, 5, 64, 100, 16) == 256 + 3 * 5 * 7 * 68 * 4
     # balanced split: a 16-byte entry per sequence (padded to 256 bytes) + 2 records per range and head
     assert P.pa_decode_workspace_size(256, 32, 128, 4096, 0) == 4096 + 256 * 32 * 2 * 132 * 4
     assert P.pa_decode_workspace_size(1, 8, 64, 0, 0) == 256 + 256 * 8 * 2 * 68 * 4
