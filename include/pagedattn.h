@@ -126,7 +126,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  *                 with num_heads == num_kv_heads and at least 1024 pairs the
  *                 library picks a partition size (512 tokens, or more where
  *                 the records would not fit this workspace) and runs the
- *                 split below; lengths above max_seq_len then give NaN rows.
+ *                 split below; a length above max_seq_len breaks the contract
+ *                 (its row is NaN once it runs past the partitions).
  *                 > 0: split context into partitions of this many tokens (a
  *                 multiple of block_size); a second kernel merges partitions
  *                 with log-sum-exp weights.  Needs a workspace.

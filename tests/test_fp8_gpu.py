@@ -97,15 +97,100 @@ def test_fp8_decode_8b_batch_full_size():
 
 
 def test_fp8_decode_13b_batch_full_size():
-    """64 sequences x 40 heads without grouping: every row, on the balanced
-    split (matrix cores) and with 512-token partitions (the vector-ALU core
-    reading the fp8 codes)."""
+    """64 sequences x 40 heads without grouping: every row, with the partitions
+    the library picks and with 512-token partitions (both on the vector-ALU
+    core fed from the work queue, reading the fp8 codes)."""
     wl = W.make_config(2, 0, poison=True)
     kc8, vc8 = _fp8_case(wl, 34)
     ref = _ref_fp8(wl, kc8, vc8)
     for ps in (0, 512):
         g = _run_fp8(wl, kc8, vc8, ps)
         assert_parity(g, ref, wl.dtype, f"fp8 13B batch ps={ps}, every sequence")
+
+
+@pytest.mark.parametrize("Hkv", [5, 6, 10])
+def test_fp8_mha_queue_head_groups(Hkv):
+    """Without grouping, fp8 pools take workgroups of up to 4 kv heads fed from
+    the work queue; 5, 6 and 10 kv heads give 1, 3 and 2 heads per workgroup.
+    16-token partitions make many items per sequence, empty ones included."""
+    seed = 900 + Hkv
+    wl = W.make_random(seed, len(EDGE_LENS), Hkv, Hkv, 128, "f16", EDGE_LENS, extra_table_cols=3)
+    kc8, vc8 = _fp8_case(wl, seed)
+    ref = _ref_fp8(wl, kc8, vc8)
+    for ps in (16, 64):
+        g = _run_fp8(wl, kc8, vc8, ps)
+        assert_parity(g, ref, "f16", f"fp8 MHA {Hkv} heads ps={ps}")
+
+
+def test_fp8_mha_queue_library_partitions():
+    """1024 (sequence, kv head) pairs without a partition size: the library
+    cuts partitions, doubling 512 tokens until the records fit the workspace
+    sized for partition_size 0 (256 seqs up to 4096 tokens: 2048-token
+    partitions; with max_seq_len 2048: 1024).  Sequences longer than the
+    partitions cover (max_seq_len 2048 passed) break the contract and give NaN
+    rows; the others are unaffected."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 300, size=256)
+    lens[[3, 100, 255]] = [4096, 2049, 2048]
+    lens[[7, 8]] = [0, 16]
+    wl = W.make_random(78, 256, 4, 4, 64, "bf16", lens, extra_table_cols=1)
+    kc8, vc8 = _fp8_case(wl, 78)
+    need = P.pa_decode_workspace_size(256, 4, 64, 4096, 0)
+    for msl, bad in ((4096, []), (2048, [3, 100])):
+        ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # stale contents must not matter
+        q = wl.query.cuda()
+        out = torch.empty_like(q)
+        P.paged_attention_decode_fp8(out, q, kc8.cuda(), vc8.cuda(), torch.from_numpy(wl.block_tables).cuda(),
+                                     torch.from_numpy(wl.seq_lens).cuda(), wl.scale, K_SCALE, V_SCALE,
+                                     partition_size=0, max_seq_len=msl, workspace=ws)
+        torch.cuda.synchronize()
+        g = out.cpu().double().numpy()
+        good = [s for s in range(256) if s not in bad]
+        assert_parity(g[good], _ref_fp8(wl, kc8, vc8)[good], "bf16", f"fp8 MHA library partitions msl={msl}")
+        for s in bad:
+            assert np.isnan(g[s]).all()
+
+
+def test_fp8_mha_queue_graph_replays():
+    """The queued launch (counter reset, decode, reduce) captured in a HIP graph
+    replays to the eager bytes, with eager work between replays."""
+    wl = W.make_config(2, 1, poison=True)
+    kc8, vc8 = _fp8_case(wl, 35)
+    q = wl.query.cuda()
+    dk, dv = kc8.cuda(), vc8.cuda()
+    bt, sl = torch.from_numpy(wl.block_tables).cuda(), torch.from_numpy(wl.seq_lens).cuda()
+    ws = torch.empty(P.pa_decode_workspace_size(wl.num_seqs, wl.num_heads, wl.head_size, wl.max_seq_len, 0),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def step(o=out):
+        P.paged_attention_decode_fp8(o, q, dk, dv, bt, sl, wl.scale, K_SCALE, V_SCALE, partition_size=0,
+                                     max_seq_len=wl.max_seq_len, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    ref = _ref_fp8(wl, kc8, vc8)
+    queries = [wl.query.cuda().clone()] + [W.random_rows(2, 60 + i, tuple(q.shape), wl.dtype).cuda()
+                                          for i in range(2)]
+    for i, qi in enumerate(queries + queries[:1]):
+        print(f"fp8 13B graph replay {i}", flush=True)
+        q.copy_(qi)
+        eager = torch.empty_like(out)
+        step(eager)
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        if i == 0 or i == len(queries):
+            assert_parity(out.cpu().double().numpy(), ref, wl.dtype, f"fp8 13B graph replay {i} vs oracle")
 
 
 def test_fp8_copy_blocks_bit_exact():
