@@ -124,7 +124,7 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  *                 least 1024 (sequence, kv head) pairs (the workspace is
  *                 still required).  Over fp8 pools (paged_attention_decode_fp8)
  *                 with num_heads == num_kv_heads and at least 1024 pairs the
- *                 library picks a partition size (512 tokens, or more where
+ *                 library picks a partition size (256 tokens, or more where
  *                 the records would not fit this workspace) and runs the
  *                 split below; a length above max_seq_len breaks the contract
  *                 (its row is NaN once it runs past the partitions).

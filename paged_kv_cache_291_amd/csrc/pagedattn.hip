@@ -315,13 +315,13 @@ int launch_valu(const Args& a, hipStream_t st) {
 // (sequence, kv head[, partition]) (13B-shaped batch, 64 seqs x 40 heads:
 // 250.6 us; fed from the work queue with 512-token partitions 262 us).  Over
 // fp8 pools, where a wave's share of a block is half as large, the work queue
-// with partitions wins: 144.9 us (512-token partitions chosen here) and 145.3
-// us (partition_size 512), against 150.4 us for the balanced split on the
-// matrix cores and 157.2 us for one workgroup per item.  Both need enough
-// (sequence, kv head) items to keep every CU busy; fewer take the balanced
-// split on the matrix cores.
+// with partitions wins: 142.1 us with the 256-token partitions chosen here
+// (512: 144.9, 1024: 158) and 145.3 us with partition_size 512, against 150.4
+// us for the balanced split on the matrix cores and 157.2 us for one
+// workgroup per item.  Both need enough (sequence, kv head) items to keep
+// every CU busy; fewer take the balanced split on the matrix cores.
 constexpr long long kValuMhaMinItems = 1024;
-constexpr int kValuPartTokens = 512;
+constexpr int kValuPartTokens = 256;
 
 // Partition size of the queue-fed vector-ALU launch for partition_size 0
 // (0: the records would not fit at any size; the caller takes another path).

@@ -124,7 +124,7 @@ def test_fp8_mha_queue_head_groups(Hkv):
 
 def test_fp8_mha_queue_library_partitions():
     """1024 (sequence, kv head) pairs without a partition size: the library
-    cuts partitions, doubling 512 tokens until the records fit the workspace
+    cuts partitions, doubling 256 tokens until the records fit the workspace
     sized for partition_size 0 (256 seqs up to 4096 tokens: 2048-token
     partitions; with max_seq_len 2048: 1024).  Sequences longer than the
     partitions cover (max_seq_len 2048 passed) break the contract and give NaN
