@@ -108,7 +108,9 @@ __device__ inline void widen_chunk(const u32x4& v, float* f) {
 // num_items).  Otherwise the grid is at most what the GPU holds at once (grid
 // <= num_items): workgroup b starts with item b, then takes item gridDim.x +
 // atomicAdd(queue, 1), fetched while the current one streams, until they run
-// out; *queue must be 0 at launch.  The hardware dispatcher hands workgroups
+// out; *queue must be 0 at launch.  order: nullptr, or the sequence each
+// item's sequence index stands for (a permutation), so that the grid can run
+// the longest sequences first.  The hardware dispatcher hands workgroups
 // to the XCDs in turn, in grid order, so with items of unequal length the
 // slots of an XCD whose turn has not come stay empty; workgroups that fetch
 // their next item keep every slot busy, and one counter keeps the items in
@@ -123,7 +125,7 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
                       const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                       int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
                       float qk_scale, float v_scale, int part_tokens, int num_parts, float* __restrict__ ws,
-                      int num_items, int* __restrict__ queue) {
+                      int num_items, int* __restrict__ queue, const int* __restrict__ order) {
   using C = ValuCfg<E, KV, D, G>;
   constexpr int BS = kBlockSize;
   constexpr int LPR = C::kLpr, RPI = C::kRpi, NI = C::kNi, EPL = C::kEpl;
@@ -157,7 +159,7 @@ pa_decode_valu_kernel(void* __restrict__ out, const void* __restrict__ query,
     const int kvh = (w % groups) * hpw + wv;
     w /= groups;
     const int part = w % num_parts;
-    const int s = w / num_parts;
+    const int s = order != nullptr ? order[w / num_parts] : w / num_parts;
     const int hq0 = kvh * G;                                      // first query head of the group
 
     u32x4 qv[G][C::kQw];                                          // query elements c*EPL .. c*EPL+EPL-1

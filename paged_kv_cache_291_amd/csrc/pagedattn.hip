@@ -19,7 +19,9 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "pagedattn.h"
 #include "common.h"
@@ -205,6 +207,7 @@ struct Args {
   void* ws;
   bool stream_kv, fp8_kv;
   bool queue;   // vector-ALU launch with partitions: workgroups take items from a counter
+  bool longest_first;   // vector-ALU launch without partitions: items ordered by length
 };
 
 // Sets the vector-ALU launch's work-queue counter to 0 (a kernel rather than a
@@ -213,23 +216,64 @@ __global__ void __launch_bounds__(64) pa_queue_reset_kernel(int* __restrict__ qu
   if (threadIdx.x == 0) queue[0] = 0;
 }
 
+// The sequences in decreasing order of their block count (ties in any order;
+// out-of-contract lengths count none, counts from kOrderBuckets - 1 on count
+// alike).  One workgroup: counts per block count in LDS, their running sums,
+// then each sequence takes the next place of its count.
+constexpr int kOrderBuckets = 4096;
+__global__ void __launch_bounds__(1024)
+pa_order_by_length_kernel(const int* __restrict__ seq_lens, int num_seqs, int max_blocks, int* __restrict__ order) {
+  __shared__ int cnt[kOrderBuckets];           // index kOrderBuckets - 1 - blocks: longest first
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < kOrderBuckets; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  auto slot = [&](int s) {
+    const int L = seq_lens[s];
+    const long long nb = (L > 0 && (long long)L <= (long long)max_blocks * kBlockSize) ? ceil_div(L, kBlockSize) : 0;
+    return kOrderBuckets - 1 - (int)(nb < kOrderBuckets - 1 ? nb : kOrderBuckets - 1);
+  };
+  for (int s = tid; s < num_seqs; s += blockDim.x) atomicAdd(&cnt[slot(s)], 1);
+  __syncthreads();
+  // exclusive running sums: thread t owns entries 4t .. 4t + 3
+  static_assert(kOrderBuckets == 4 * 1024, "four entries per thread");
+  int v[4], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { v[j] = cnt[4 * tid + j]; tot += v[j]; }
+  int inc = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int base = inc - tot;
+  for (int w2 = 0; w2 < wv; ++w2) base += wsum[w2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { cnt[4 * tid + j] = base; base += v[j]; }
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += blockDim.x) order[atomicAdd(&cnt[slot(s)], 1)] = s;
+}
+
 // Workgroups of `kernel` (`threads` lanes, no dynamic LDS) the current device
-// holds at once; found once per device and kernel (one workgroup size per
-// kernel), 0 if the runtime cannot tell.
-template <class K>
-int resident_workgroups(K kernel, int threads) {
-  static std::atomic<int> cached[64];
+// holds at once, found once per (kernel, workgroup size, device); 0 if the
+// runtime cannot tell.
+int resident_workgroups(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int>, int> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n > 0) return n;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_tuple(kernel, threads, dev);
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
     return 0;
-  n = cus * per_cu;
-  cached[dev].store(n, std::memory_order_relaxed);
-  return n;
+  cache[key] = cus * per_cu;
+  return cus * per_cu;
 }
 
 template <class E, class KV, int D, int G, bool NT>
@@ -288,11 +332,17 @@ int launch_valu(const Args& a, hipStream_t st) {
   auto k = a.stream_kv ? pa_decode_valu_kernel<E, KV, D, G, true> : pa_decode_valu_kernel<E, KV, D, G, false>;
   long long grid = items;
   int* queue = nullptr;
+  int* order = nullptr;
   float* ws = nullptr;
   if (a.part_tokens > 0) ws = reinterpret_cast<float*>(static_cast<char*>(a.ws) + kQueueHeaderBytes);
+  if (a.longest_first && a.part_tokens == 0) {
+    order = static_cast<int*>(a.ws);
+    hipLaunchKernelGGL(pa_order_by_length_kernel, dim3(1), dim3(1024), 0, st, a.sl, a.num_seqs, a.max_blocks, order);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
   if (queued) {
     queue = static_cast<int*>(a.ws);
-    int slots = resident_workgroups(k, 64 * hpw);
+    int slots = resident_workgroups(reinterpret_cast<const void*>(k), 64 * hpw);
     if (slots <= 0) slots = kSkWorkgroups * 4 * ValuOccupancy<E, KV, D, G>::kWaves / hpw;
     grid = items < slots ? items : slots;
     hipLaunchKernelGGL(pa_queue_reset_kernel, dim3(1), dim3(64), 0, st, queue);
@@ -300,7 +350,7 @@ int launch_valu(const Args& a, hipStream_t st) {
   }
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                      a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                     a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, ws, (int)items, queue);
+                     a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, ws, (int)items, queue, order);
   if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   if (a.part_tokens > 0) {
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
@@ -312,8 +362,12 @@ int launch_valu(const Args& a, hipStream_t st) {
 
 // One query head per kv head (no grouping) leaves the matrix-core tile 1/16
 // dense; there the vector-ALU core runs.  Over 16-bit pools one workgroup per
-// (sequence, kv head[, partition]) (13B-shaped batch, 64 seqs x 40 heads:
-// 250.6 us; fed from the work queue with 512-token partitions 262 us).  Over
+// (sequence, kv head[, partition]); without partitions the sequences are
+// first ordered longest first, so that the longest items (one wave streams a
+// 2036-token sequence for ~230 us) start at once and short ones fill in
+// behind them (13B-shaped batch, 64 seqs x 40 heads, lengths 128..2048: 234.2
+// us, in the order given 251.5 us; fed from the work queue with 512-token
+// partitions 262 us).  Over
 // fp8 pools, where a wave's share of a block is half as large, the work queue
 // with partitions wins: 142.1 us with the 256-token partitions chosen here
 // (512: 144.9, 1024: 158) and 145.3 us with partition_size 512, against 150.4
@@ -352,8 +406,12 @@ int launch(const Args& a, hipStream_t st) {
     return a.stream_kv ? launch_mfma<E, KvFp8, D, G, true>(a, st) : launch_mfma<E, KvFp8, D, G, false>(a, st);
   } else {
     if constexpr (G == 1) {
-      if (a.part_tokens > 0 || (long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems)
-        return launch_valu<E, Kv16, D, G>(a, st);
+      if (a.part_tokens > 0) return launch_valu<E, Kv16, D, G>(a, st);
+      if ((long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems) {
+        Args b = a;
+        b.longest_first = true;
+        return launch_valu<E, Kv16, D, G>(b, st);
+      }
     }
     return a.stream_kv ? launch_mfma<E, Kv16, D, G, true>(a, st) : launch_mfma<E, Kv16, D, G, false>(a, st);
   }

@@ -101,6 +101,25 @@ def test_mha_vector_core_sweep(dtype, D, ps):
     assert torch.equal(shared, out)
 
 
+def test_mha_vector_core_longest_first_order():
+    """Without partitions the 16-bit vector-ALU launch first orders the
+    sequences by block count (one workgroup: counts, running sums, places).
+    2100 sequences (several passes of its 1024 threads), zero lengths, equal
+    counts, and one sequence of 4125 blocks, past the counts it tells apart:
+    every row against the oracle."""
+    rng = np.random.default_rng(2100)
+    lens = rng.integers(1, 200, size=2100)
+    lens[[0, 9, 2099]] = 0
+    lens[[10, 11, 12]] = 33
+    lens[1500] = 66000
+    wl = W.make_random(2100, 2100, 1, 1, 64, "bf16", lens, pool_factor=1.2)
+    assert wl.num_seqs * wl.num_kv_heads >= 1024
+    out, _ = gpu_decode(wl, partition_size=0)
+    g = out.double().numpy()
+    assert_parity(g, oracle_decode(wl), "bf16", "2100 sequences, longest first")
+    assert (g[[0, 9, 2099]] == 0).all()
+
+
 @pytest.mark.parametrize("ps", [0, 16])
 def test_mha_vector_core_contract_violations(ps):
     """Out-of-contract lengths and ids on the 16-bit vector-ALU path: NaN
