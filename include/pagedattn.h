@@ -209,8 +209,9 @@ int paged_attention_decode_noalloc(void* out, const void* query, const void* k_c
  * a second kernel merges partial results (needs the workspace; with two
  * tiles the K/V loads use the default cache policy whatever flags says,
  * since two waves read each line); otherwise two tiles per wave and 16 per
- * workgroup sharing K/V through LDS, or, for one tile (more than 16383
- * sequences), one wave per tile.
+ * workgroup sharing K/V through LDS (from 32 sequences on, run longest
+ * sequence first, which needs the workspace), or, for one tile (more than
+ * 16383 sequences), one wave per tile.
  * Rows of a sequence with n_s > seq_lens[s], a length past its table row or a
  * block id outside the pool are NaN.  Rows beyond max_query_len are not
  * written.
@@ -225,7 +226,9 @@ int paged_attention_prefill(void* out, const void* query, const void* k_cache, c
 /* Workspace bytes paged_attention_prefill(_fp8) needs with these sizes (0:
  * none):  round_up(num_seqs * 16, 256) + 256 * num_kv_heads * 2 * 16 * tiles *
  * (head_size + 4) * 4 on the split path, tiles = ceil(max_query_len *
- * (num_heads / num_kv_heads) / 16), else 0.  0 for invalid sizes. */
+ * (num_heads / num_kv_heads) / 16); round_up(num_seqs * 4, 256) (the
+ * longest-first order) on the LDS path with at least 32 sequences; else 0.
+ * 0 for invalid sizes. */
 size_t pa_prefill_workspace_size(int num_seqs, int num_query_tokens, int num_heads, int num_kv_heads,
                                  int head_size, int max_query_len);
 

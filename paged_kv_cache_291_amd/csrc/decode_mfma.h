@@ -866,7 +866,8 @@ constexpr int kPfSmallGroupTiles = 8;
 // (the buffer range of the block is cut to its valid rows).  The linear
 // workgroup id is split so that all workgroups of one (sequence, kv head)
 // land on the same XCD (workgroups are dealt to the 8 XCDs round robin),
-// where its K/V stay in that XCD's L2.
+// where its K/V stay in that XCD's L2.  order: nullptr, or the sequence each
+// sequence index stands for (a permutation: longest first).
 template <class E, class KV, int D, int G, bool NT, int TW, int TPG>
 __global__ void __launch_bounds__(64 * TPG / TW)
 __attribute__((amdgpu_waves_per_eu(TW == 4 ? 1 : 2, TW == 4 ? 1 : 8)))
@@ -874,7 +875,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
                       const char* __restrict__ v_cache, const int* __restrict__ block_tables,
                       const int* __restrict__ seq_lens, const int* __restrict__ query_start, int num_seqs,
                       int num_heads, int num_kv_heads, int max_blocks, int num_blocks, int groups_per_pair,
-                      float qk_scale, float v_scale) {
+                      float qk_scale, float v_scale, const int* __restrict__ order) {
   using SH = MfmaShape<D>;
   using M = Mfma<E>;
   constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe;
@@ -895,7 +896,8 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int pair = (slot / groups_per_pair) * 8 + xcd, grp = slot % groups_per_pair;
   if (pair >= num_seqs * num_kv_heads) return;
-  const int s = pair / num_kv_heads, kvh = pair - s * num_kv_heads;
+  const int si = pair / num_kv_heads, kvh = pair - si * num_kv_heads;
+  const int s = order != nullptr ? order[si] : si;
   const int q0 = query_start[s], n = query_start[s + 1] - q0, L = seq_lens[s];
   const int wg_tok0 = grp * TPG * TPT;
   if (n <= 0 || wg_tok0 >= n) return;                // the whole workgroup: uniform

@@ -180,8 +180,9 @@ def test_prefill_host_errors():
     # up to 2 tiles of 16 rows per kv head stay on the split (16 * tiles record rows per kv head)
     assert P.pa_prefill_workspace_size(256, 2048, 32, 8, 128, 8) == 4096 + 256 * 8 * 2 * 32 * 132 * 4
     assert P.pa_prefill_workspace_size(256, 1280, 32, 8, 128, 5) == 4096 + 256 * 8 * 2 * 32 * 132 * 4
-    assert P.pa_prefill_workspace_size(256, 2304, 32, 8, 128, 9) == 0
-    assert P.pa_prefill_workspace_size(256, 4096, 32, 8, 128, 16) == 0
+    assert P.pa_prefill_workspace_size(256, 2304, 32, 8, 128, 9) == 1024     # LDS path: the longest-first order
+    assert P.pa_prefill_workspace_size(256, 4096, 32, 8, 128, 16) == 1024
+    assert P.pa_prefill_workspace_size(31, 496, 32, 8, 128, 16) == 0         # fewer than 32 sequences: no order
 
 
 def test_python_binding_refuses_host_tensors():

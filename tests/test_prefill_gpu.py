@@ -154,6 +154,32 @@ def test_prefill_contract_violations_give_nan_rows(D, nq):
     assert_parity(g[:3], ref[:3], "bf16", "rows beside the out-of-contract ones")
 
 
+def test_many_tile_longest_first_contract_violations():
+    """40 sequences (the many-tile kernel orders them longest first): zero
+    query rows, equal lengths, and out-of-contract sequences (more query rows
+    than tokens, a length past the table row, an id outside the pool) give NaN
+    rows; every other row against the oracle."""
+    rng = np.random.default_rng(40)
+    lens = rng.integers(12, 300, size=40).tolist()
+    lens[5] = lens[6] = lens[7] = 77
+    nq = [12] * 40
+    nq[8], nq[9] = 0, 9
+    wl, starts, q = _case(73, 16, 4, 128, "bf16", lens, nq)
+    bt, sl = wl.block_tables.copy(), wl.seq_lens.copy()
+    sl[1] = 3
+    sl[2] = bt.shape[1] * 16 + 1
+    bt[3, 1] = wl.num_blocks
+    g = _gpu(wl, starts, q, bt=bt, sl=sl)
+    bad = [1, 2, 3]
+    for s in bad:
+        assert np.isnan(g[starts[s]:starts[s + 1]]).all(), s
+    good = [s for s in range(40) if s not in bad]
+    ref = oracle.paged_prefill_ref(W.raw_numpy(q), W.raw_numpy(wl.k_cache), W.raw_numpy(wl.v_cache),
+                                   wl.block_tables, wl.seq_lens, starts, wl.scale, "bf16", seqs=good)
+    rows = np.concatenate([np.arange(starts[s], starts[s + 1]) for s in good])
+    assert_parity(g[rows], ref[rows], "bf16", "many-tile, 40 sequences longest first, beside out-of-contract ones")
+
+
 def test_chunked_prefill_batch_full_size():
     """8 sequences of 4096 tokens whose last 512 are the query chunk (8B head
     shape): every row against the oracle."""
@@ -228,11 +254,12 @@ def test_few_rows_many_segments_fp8_pools(dtype, Hq, Hkv, max_q):
     assert_parity(g, ref, dtype, f"{S} short sequences over fp8 pools {dtype} {Hq}/{Hkv} up to {max_q} rows")
 
 
-@pytest.mark.parametrize("nqv", [4, 8])
+@pytest.mark.parametrize("nqv", [4, 8, 16])
 def test_verify_8b_batch_full_size(nqv):
     """Speculative verification on the 8B-shaped batch (4 or 8 query rows per
-    sequence: one or two 16-row tiles per kv head): the balanced split with
-    causal rows, every row against the oracle."""
+    sequence: one or two 16-row tiles per kv head, the balanced split with
+    causal rows; 16: four tiles, the many-tile kernel run longest sequence
+    first), every row against the oracle."""
     wl = W.make_config(3, 0, poison=True)
     S = wl.num_seqs
     nq = np.full(S, nqv, np.int32)
