@@ -147,7 +147,7 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, cfg: int, partition: i
             name = r["Kernel_Name"]
             if "pa::" not in name or "scatter" in name:
                 continue
-            short = name.split("<")[0].split("::")[-1]
+            short = name.replace("(anonymous namespace)::", "").split("<")[0].split("(")[0].split("::")[-1]
             step.setdefault(short, []).append(float(r["Counter_Value"]))
         out[counter] = (calib_kib, {k: sum(v) / len(v) for k, v in step.items()})
     return out
@@ -455,7 +455,8 @@ def bench_prefill(args):
         "roofline": ({"bound": "hbm", "achieved": round(kv / launch / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(kv / launch / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                       "kernel": ("pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel"
-                                 if mq * (wl.num_heads // wl.num_kv_heads) <= 32 else "pa_prefill_lds_kernel"),
+                                 if mq * (wl.num_heads // wl.num_kv_heads) <= 32 else
+                                 "pa_prefill_lds_kernel" + ("+pa_order_by_length_kernel" if wl.num_seqs >= 32 else "")),
                       "bytes_per_launch": kv}
                      if args.prefill_case == "verify" else
                      {"bound": "mfma", "achieved": round(flops / launch / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -698,8 +699,12 @@ def bench_decode(args):
     # query head per kv head (with partitions, or from 1024 (sequence, kv
     # head) pairs; over fp8 pools then cut into partitions by the library)
     mha = wl.num_heads == wl.num_kv_heads and (ps > 0 or wl.num_seqs * wl.num_kv_heads >= 1024)
-    if wl.dtype == "f32" or mha:
-        kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 or (fp8 and mha) else "")
+    if wl.dtype == "f32":
+        kernel = "pa_decode_valu_kernel" + ("+pa_reduce_kernel" if ps > 0 else "")
+    elif mha and fp8:                                  # fed from the work queue, partitions merged
+        kernel = "pa_decode_valu_kernel+pa_reduce_kernel+pa_queue_reset_kernel"
+    elif mha:                                          # partitions merged, or longest sequence first
+        kernel = "pa_decode_valu_kernel+" + ("pa_reduce_kernel" if ps > 0 else "pa_order_by_length_kernel")
     else:
         kernel = "pa_decode_mfma_kernel+pa_reduce_kernel" if ps > 0 else "pa_decode_sk_kernel+pa_sk_merge_kernel"
     if fp8:

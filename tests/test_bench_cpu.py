@@ -69,6 +69,20 @@ def test_traffic_from_counters_scales_by_the_calibration_copy(tmp_path, monkeypa
     assert bench.traffic_for("pa_decode_sk_kernel+pa_sk_merge_kernel", "cfg3") is None
 
 
+def test_traffic_keys_strip_template_arguments_and_parameters(tmp_path, monkeypatch):
+    va = "void pa::pa_decode_valu_kernel<pa::ElemF16, pa::Kv16, 128, 1, true>(void*, int*)"
+    order = "pa::(anonymous namespace)::pa_order_by_length_kernel(int const*, int, int, int*)"
+    cp = "__amd_rocclr_copyBuffer"
+    _counter_run(tmp_path / "f", "FETCH_SIZE", [(va, 1000), (order, 2), (cp, 524288)])
+    _counter_run(tmp_path / "w", "WRITE_SIZE", [(va, 10), (order, 1), (cp, 1048576)])
+    tj = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(tj))
+    args = types.SimpleNamespace(traffic_from=f"{tmp_path / 'f'},{tmp_path / 'w'}", config=2, partition=-1,
+                                 flags=-1, copy_calibration=1024)
+    bench.write_traffic(args)
+    assert list(json.load(open(tj))) == ["pa_decode_valu_kernel+pa_order_by_length_kernel|cfg2"]
+
+
 @pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})])
 def test_more_than_one_gpu_is_refused(argv, env):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
