@@ -445,6 +445,10 @@ __device__ __forceinline__ void mfma_finish(const MfmaState<D>& st, bool bad, vo
 // flushed to HBM in the middle of the K/V stream (8 x 32k tokens, 64/8
 // heads: 185 -> 172 us).
 // ws: partial records [num_seqs * num_heads * num_parts].
+// queue (or nullptr): as in the vector-ALU launch, the grid is at most what
+// the GPU holds at once and a workgroup takes its next item from the counter
+// (thread 0 fetches it when the item starts; it reaches the other waves
+// through LDS at the item's end, before its stores).
 template <class E, class KV, int D, int G, bool NT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
@@ -452,18 +456,36 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
                       const int* __restrict__ block_tables, const int* __restrict__ seq_lens,
                       int num_heads, int num_kv_heads, int max_blocks, int num_blocks,
                       float qk_scale, float v_scale, int part_tokens, int num_parts, int hpw,
-                      int num_items, float* __restrict__ ws) {
+                      int num_items, float* __restrict__ ws, int* __restrict__ queue) {
   constexpr int BS = kBlockSize;
   constexpr int REC = rec_floats<D>();
+  __shared__ int s_tk[2];
   const int lane = threadIdx.x & 63;
   const int groups = num_kv_heads / hpw;
   const int64_t cap = min((int64_t)max_blocks * BS, (int64_t)num_parts * part_tokens);
+  const bool queued = queue != nullptr;
+  // 0, but not known to the compiler to be uniform (see the vector-ALU launch)
+  int* const counter = queued ? queue + (int)__builtin_amdgcn_mbcnt_lo(0u, 0u) : nullptr;
 
   MfmaState<D> held;                          // the previous item's record, not yet written
   bool held_bad = false, have_held = false;
   float* held_rec = nullptr;
   int64_t held_row0 = 0;
-  for (int64_t item = blockIdx.x; item < num_items; item += gridDim.x) {   // 64-bit: item + grid may pass 2^31
+  int parity = 0;
+  for (int64_t item = blockIdx.x; item < num_items;) {   // 64-bit: item + grid may pass 2^31
+    int tk = 0;
+    if (queued && threadIdx.x == 0) tk = atomicAdd(counter, 1);
+    auto next_item = [&]() {
+      if (queued) {
+        asm volatile("" : "+v"(tk) :: "memory");
+        if (threadIdx.x == 0) s_tk[parity] = __builtin_amdgcn_readfirstlane(tk);
+        __syncthreads();
+        item = (int64_t)gridDim.x + s_tk[parity];
+        parity ^= 1;
+      } else {
+        item += gridDim.x;
+      }
+    };
     int w = (int)item;
     const int kvh = (w % groups) * hpw + (int)(threadIdx.x >> 6);
     w /= groups;
@@ -474,7 +496,10 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
     const int L = seq_lens[s];
     const bool bad_len = L < 0 || (int64_t)L > cap;
     const int nparts_seq = bad_len ? 1 : ceil_div(L, part_tokens);
-    if (part >= (nparts_seq > 0 ? nparts_seq : 1)) continue;   // empty partition
+    if (part >= (nparts_seq > 0 ? nparts_seq : 1)) {          // empty partition
+      next_item();
+      continue;
+    }
     const bool final_write = nparts_seq <= 1;
 
     MfmaState<D> st;
@@ -486,6 +511,7 @@ pa_decode_mfma_kernel(void* __restrict__ out, const void* __restrict__ query,
       bad = mfma_segment<E, KV, D, NT, true>(st, k_cache, v_cache, block_tables + (int64_t)s * max_blocks,
                                              t_begin / BS, ceil_div(t_end, BS), t_end, num_blocks, num_kv_heads,
                                              kvh, qk_scale, lane);
+    next_item();
     if (have_held) {
       mfma_finish<E, D, G>(held, held_bad, out, held_row0, held_rec, (int64_t)num_parts * REC, v_scale, lane);
       have_held = false;

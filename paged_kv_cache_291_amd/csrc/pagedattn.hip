@@ -37,6 +37,8 @@ namespace {
 constexpr int kSkWorkgroups = 256;
 // Largest batch the balanced split handles (its prefix sums live in LDS).
 constexpr int kSkMaxSeqs = 16383;
+// Most kv heads per workgroup of the queue-fed fixed split on the matrix cores.
+constexpr int kMfmaQueueHeads = 8;
 // Multi-token queries off the balanced split: from this many 16-row query
 // tiles per (sequence, kv head) on, the tiles share each K/V block through
 // LDS (16 per workgroup); one tile runs one wave per tile (8B batch, 5..8
@@ -279,22 +281,36 @@ int resident_workgroups(const void* kernel, int threads) {
 template <class E, class KV, int D, int G, bool NT>
 int launch_mfma(const Args& a, hipStream_t st) {
   if (a.part_tokens > 0) {
-    const int hpw = heads_per_workgroup(a.num_kv_heads);
-    const long long items = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
+    int hpw = heads_per_workgroup(a.num_kv_heads);
+    long long items = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
     if (items > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     const int groups = a.num_kv_heads / hpw;
     // Up to two items per CU: one round of at most one workgroup per CU,
     // workgroup b taking items b and b + grid (grid a multiple of the head
     // groups, so both are of its head group), the first item's record held
-    // until the second has streamed.  More items: one per workgroup, and the
-    // dispatcher fills the CUs round by round (pairing them would leave a
-    // half-empty last round whenever the rounds are odd in number).
+    // until the second has streamed.  More items: workgroups of up to
+    // kMfmaQueueHeads kv heads, as many as the GPU holds, take them from the
+    // work queue (the dispatcher's in-order deal over the XCDs left slots
+    // empty with items of unequal length).
     const long long wgs = kSkWorkgroups >= groups ? kSkWorkgroups / groups * groups : groups;
-    const long long grid = items <= 2 * wgs ? (items < wgs ? items : wgs) : items;
+    long long grid = items <= 2 * wgs ? (items < wgs ? items : wgs) : items;
     float* ws = reinterpret_cast<float*>(static_cast<char*>(a.ws) + kQueueHeaderBytes);
-    hipLaunchKernelGGL((pa_decode_mfma_kernel<E, KV, D, G, NT>), dim3((unsigned)grid), dim3(64 * hpw), 0, st,
+    int* queue = nullptr;
+    auto k = pa_decode_mfma_kernel<E, KV, D, G, NT>;
+    if (items > 2 * wgs) {
+      hpw = heads_per_workgroup(a.num_kv_heads, kMfmaQueueHeads);
+      items = (long long)a.num_seqs * a.num_parts * (a.num_kv_heads / hpw);
+      if (items > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+      queue = static_cast<int*>(a.ws);
+      int slots = resident_workgroups(reinterpret_cast<const void*>(k), 64 * hpw);
+      if (slots <= 0) slots = kSkWorkgroups * 8 / hpw;
+      grid = items < slots ? items : slots;
+      hipLaunchKernelGGL(pa_queue_reset_kernel, dim3(1), dim3(64), 0, st, queue);
+      if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * hpw), 0, st,
                        a.out, a.query, a.kc, a.vc, a.bt, a.sl, a.num_heads, a.num_kv_heads, a.max_blocks,
-                       a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, hpw, (int)items, ws);
+                       a.num_blocks, a.qk_scale, a.v_scale, a.part_tokens, a.num_parts, hpw, (int)items, ws, queue);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     hipLaunchKernelGGL((pa_reduce_kernel<E, D>), dim3((unsigned)(a.num_seqs * a.num_heads)), dim3(64), 0, st,
                        a.out, ws, a.sl, a.num_heads, a.max_blocks, a.part_tokens, a.num_parts);
