@@ -431,6 +431,11 @@ def bench_prefill(args):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
     mq = int(nq.max())
+    # the library's path: the balanced split for one 16-row tile per kv head, and
+    # for two while the batch has fewer than 32 sequences or 1024 (sequence, kv
+    # head) pairs; else the many-tile LDS kernel (longest first from 32 sequences)
+    rows = mq * (wl.num_heads // wl.num_kv_heads)
+    split = rows <= 16 or (rows <= 32 and not (wl.num_seqs >= 32 and wl.num_seqs * wl.num_kv_heads >= 1024))
 
     def step():
         P.paged_attention_prefill(out, q, kc, vc, bt, sl, qs, wl.scale, max_query_len=mq, stream=stream)
@@ -454,8 +459,7 @@ def bench_prefill(args):
         "us_per_step": round(wall * 1e6, 2), "us_per_step_flushed": dist, "launch_us": round(launch * 1e6, 2),
         "roofline": ({"bound": "hbm", "achieved": round(kv / launch / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": round(kv / launch / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                      "kernel": ("pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel"
-                                 if mq * (wl.num_heads // wl.num_kv_heads) <= 32 else
+                      "kernel": ("pa_decode_sk_kernel(multi-token rows)+pa_sk_merge_mq_kernel" if split else
                                  "pa_prefill_lds_kernel" + ("+pa_order_by_length_kernel" if wl.num_seqs >= 32 else "")),
                       "bytes_per_launch": kv}
                      if args.prefill_case == "verify" else

@@ -661,16 +661,24 @@ int launch_mq_split(void* out, const void* query, const void* kc, const void* vc
 }
 
 // Which path a multi-token call takes, and the workspace it needs.
-bool prefill_uses_split(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
-  return mq_tiles(num_heads, num_kv_heads, max_q) <= kSkMaxTiles && num_seqs <= kSkMaxSeqs;
-}
-
 // The many-tile kernel's grid runs the sequences longest first when there are
 // at least kOrderMinSeqs of them (the order takes 4 bytes per sequence of the
 // workspace): 8B batch, 256 sequences, 16 / 12 query tokens each: 293.7 /
 // 288.0 us against 352.0 / 343.5 us in the order given.  A few sequences (a
 // chunked prefill) gain nothing from it and would pay for the extra kernel.
+// So ordered, it also beats the balanced split for two tiles per kv head
+// once the (sequence, kv head) pairs fill the GPU (5 / 8 tokens: 274.3 /
+// 282.3 us against 287.9 / 299.0 us), though three of its four waves then
+// only stage blocks; smaller batches (few long sequences) keep the split.
 constexpr int kOrderMinSeqs = 32;
+constexpr long long kLdsTwoTileMinPairs = 1024;
+
+bool prefill_uses_split(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
+  const int tiles = mq_tiles(num_heads, num_kv_heads, max_q);
+  if (tiles > kSkMaxTiles || num_seqs > kSkMaxSeqs) return false;
+  return !(tiles == 2 && num_seqs >= kOrderMinSeqs && (long long)num_seqs * num_kv_heads >= kLdsTwoTileMinPairs);
+}
+
 bool prefill_longest_first(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
   return !prefill_uses_split(num_seqs, num_heads, num_kv_heads, max_q) &&
          ceil_div(max_q * (num_heads / num_kv_heads), 16) >= kPrefillLdsTiles && num_seqs >= kOrderMinSeqs;

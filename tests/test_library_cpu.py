@@ -177,9 +177,12 @@ def test_prefill_host_errors():
     assert P.pa_prefill_workspace_size(256, 1024, 32, 8, 128, 4) == 4096 + 256 * 8 * 2 * 16 * 132 * 4
     assert P.pa_prefill_workspace_size(8, 4096, 32, 8, 128, 512) == 0
     assert P.pa_prefill_workspace_size(3, 6, 8, 8, 64, 0) == 256 + 256 * 8 * 2 * 16 * 68 * 4   # 0: T = 6 rows
-    # up to 2 tiles of 16 rows per kv head stay on the split (16 * tiles record rows per kv head)
-    assert P.pa_prefill_workspace_size(256, 2048, 32, 8, 128, 8) == 4096 + 256 * 8 * 2 * 32 * 132 * 4
-    assert P.pa_prefill_workspace_size(256, 1280, 32, 8, 128, 5) == 4096 + 256 * 8 * 2 * 32 * 132 * 4
+    # 2 tiles of 16 rows per kv head stay on the split (16 * tiles record rows per kv head) below 32
+    # sequences or 1024 (sequence, kv head) pairs; above, the LDS kernel runs them longest first
+    assert P.pa_prefill_workspace_size(100, 800, 4, 1, 128, 8) == 1792 + 256 * 1 * 2 * 32 * 132 * 4
+    assert P.pa_prefill_workspace_size(31, 248, 32, 8, 128, 8) == 512 + 256 * 8 * 2 * 32 * 132 * 4
+    assert P.pa_prefill_workspace_size(256, 2048, 32, 8, 128, 8) == 1024
+    assert P.pa_prefill_workspace_size(256, 1280, 32, 8, 128, 5) == 1024
     assert P.pa_prefill_workspace_size(256, 2304, 32, 8, 128, 9) == 1024     # LDS path: the longest-first order
     assert P.pa_prefill_workspace_size(256, 4096, 32, 8, 128, 16) == 1024
     assert P.pa_prefill_workspace_size(31, 496, 32, 8, 128, 16) == 0         # fewer than 32 sequences: no order

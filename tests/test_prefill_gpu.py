@@ -212,16 +212,18 @@ def test_few_query_rows_per_sequence(dtype, D, Hq, Hkv, fp8):
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 4), ("f16", 64, 8, 2), ("bf16", 16, 16, 16),
                                                ("bf16", 32, 8, 8), ("f16", 64, 8, 4), ("bf16", 32, 8, 16),
-                                               ("bf16", 16, 16, 48), ("f16", 8, 2, 12)])
+                                               ("bf16", 16, 16, 48), ("f16", 8, 2, 12), ("bf16", 4, 1, 8),
+                                               ("f16", 8, 1, 4)])
 def test_few_rows_many_segments_per_range(dtype, Hq, Hkv, max_q):
     """Speculative verification over hundreds of short sequences, so that a
     workgroup's range holds several sequences: a first segment that began in
     an earlier range and ends inside this one (its record is held until the
     range's last segment), one that runs past the range's end as well, and
     sequences without query rows in between.  Up to 16 rows per kv head is
-    one tile per wave; 17..32 rows take two tile waves per kv head (a wave
-    whose tile has no rows of a sequence still streams its blocks); more rows
-    go to the LDS kernel.  Every row against the oracle."""
+    one tile per wave; 17..32 rows are two tiles, held by one wave per kv
+    head, where fewer than 1024 (sequence, kv head) pairs (one kv head here)
+    keep the split; more pairs, or more rows, go to the LDS kernel, which runs
+    the sequences longest first.  Every row against the oracle."""
     rng = np.random.default_rng(Hq * 10 + Hkv + max_q)
     S = 600
     lens = rng.integers(1, 200, size=S)
@@ -236,10 +238,12 @@ def test_few_rows_many_segments_per_range(dtype, Hq, Hkv, max_q):
     assert_parity(g, ref, dtype, f"{S} short sequences {dtype} {Hq}/{Hkv} up to {max_q} rows")
 
 
-@pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 8), ("f16", 64, 8, 4), ("bf16", 32, 8, 4)])
+@pytest.mark.parametrize("dtype,Hq,Hkv,max_q", [("bf16", 32, 8, 8), ("f16", 64, 8, 4), ("bf16", 32, 8, 4), ("bf16", 4, 1, 8)])
 def test_few_rows_many_segments_fp8_pools(dtype, Hq, Hkv, max_q):
-    """The few-row split over fp8 (e4m3) pools, one and two tile waves per kv
-    head, over hundreds of short sequences; every row against the oracle."""
+    """Few query rows per sequence over fp8 (e4m3) pools and hundreds of short
+    sequences: one tile per kv head on the split; two tiles on the split (one
+    kv head: fewer than 1024 pairs) or on the LDS kernel, longest first (eight
+    kv heads); every row against the oracle."""
     rng = np.random.default_rng(Hq * 20 + Hkv + max_q)
     S = 400
     lens = rng.integers(1, 200, size=S)
@@ -254,12 +258,12 @@ def test_few_rows_many_segments_fp8_pools(dtype, Hq, Hkv, max_q):
     assert_parity(g, ref, dtype, f"{S} short sequences over fp8 pools {dtype} {Hq}/{Hkv} up to {max_q} rows")
 
 
-@pytest.mark.parametrize("nqv", [4, 8, 16])
+@pytest.mark.parametrize("nqv", [4, 5, 8, 16])
 def test_verify_8b_batch_full_size(nqv):
-    """Speculative verification on the 8B-shaped batch (4 or 8 query rows per
-    sequence: one or two 16-row tiles per kv head, the balanced split with
-    causal rows; 16: four tiles, the many-tile kernel run longest sequence
-    first), every row against the oracle."""
+    """Speculative verification on the 8B-shaped batch (4 query rows per
+    sequence: one 16-row tile per kv head, the balanced split with causal
+    rows; 5 and 8: two tiles, 16: four tiles, the many-tile kernel run
+    longest sequence first), every row against the oracle."""
     wl = W.make_config(3, 0, poison=True)
     S = wl.num_seqs
     nq = np.full(S, nqv, np.int32)
