@@ -121,13 +121,16 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_size,
  *                 kernel); needs a workspace; at most 16383 sequences.  For
  *                 fp32 one pass per (sequence, kv head), no workspace; so
  *                 too for bf16/fp16 with num_heads == num_kv_heads and at
- *                 least 1024 (sequence, kv head) pairs (the workspace is
- *                 still required).  Over fp8 pools (paged_attention_decode_fp8)
- *                 with num_heads == num_kv_heads and at least 1024 pairs the
- *                 library picks a partition size (256 tokens, or more where
- *                 the records would not fit this workspace) and runs the
- *                 split below; a length above max_seq_len breaks the contract
- *                 (its row is NaN once it runs past the partitions).
+ *                 least 1024 (sequence, kv head) pairs, longest sequence
+ *                 first (the workspace is still required).  With
+ *                 num_heads == num_kv_heads otherwise (fp8 pools
+ *                 (paged_attention_decode_fp8) always, bf16/fp16 with fewer
+ *                 pairs) the library picks a partition size (256 tokens, or
+ *                 more where the records would not fit this workspace) and
+ *                 runs the split below if that makes at least 1024
+ *                 (sequence, partition, kv head) items; a length above
+ *                 max_seq_len then breaks the contract (its row is NaN once
+ *                 it runs past the partitions).
  *                 > 0: split context into partitions of this many tokens (a
  *                 multiple of block_size); a second kernel merges partitions
  *                 with log-sum-exp weights.  Needs a workspace.

@@ -392,6 +392,7 @@ int launch_valu(const Args& a, hipStream_t st) {
 // every CU busy; fewer take the balanced split on the matrix cores.
 constexpr long long kValuMhaMinItems = 1024;
 constexpr int kValuPartTokens = 256;
+constexpr bool kValuQueue16 = true;
 
 // Partition size of the queue-fed vector-ALU launch for partition_size 0
 // (0: the records would not fit at any size; the caller takes another path).
@@ -404,6 +405,18 @@ int valu_part_tokens(const Args& a, int head_size) {
   return 0;
 }
 
+// The queued vector-ALU launch with partitions the library picks, when those
+// give enough (sequence, partition, kv head) items (an upper bound: the
+// partitions max_seq_len needs, for every sequence).
+bool queued_partitions(const Args& a, int head_size, Args& b) {
+  b = a;
+  b.queue = true;
+  b.part_tokens = valu_part_tokens(a, head_size);
+  if (b.part_tokens <= 0) return false;
+  b.num_parts = split_num_parts(kBlockSize, a.max_blocks, a.max_seq_len, b.part_tokens);
+  return (long long)a.num_seqs * b.num_parts * a.num_kv_heads >= kValuMhaMinItems;
+}
+
 template <class E, int D, int G>
 int launch(const Args& a, hipStream_t st) {
   if constexpr (E::kBytes == 4) {
@@ -413,21 +426,18 @@ int launch(const Args& a, hipStream_t st) {
       Args b = a;
       b.queue = true;
       if (a.part_tokens > 0) return launch_valu<E, KvFp8, D, G>(b, st);
-      b.part_tokens = (long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems ? valu_part_tokens(a, D) : 0;
-      if (b.part_tokens > 0) {
-        b.num_parts = split_num_parts(kBlockSize, a.max_blocks, a.max_seq_len, b.part_tokens);
-        return launch_valu<E, KvFp8, D, G>(b, st);
-      }
+      if (queued_partitions(a, D, b)) return launch_valu<E, KvFp8, D, G>(b, st);
     }
     return a.stream_kv ? launch_mfma<E, KvFp8, D, G, true>(a, st) : launch_mfma<E, KvFp8, D, G, false>(a, st);
   } else {
     if constexpr (G == 1) {
       if (a.part_tokens > 0) return launch_valu<E, Kv16, D, G>(a, st);
+      Args b = a;
       if ((long long)a.num_seqs * a.num_kv_heads >= kValuMhaMinItems) {
-        Args b = a;
         b.longest_first = true;
         return launch_valu<E, Kv16, D, G>(b, st);
       }
+      if (kValuQueue16 && queued_partitions(a, D, b)) return launch_valu<E, Kv16, D, G>(b, st);
     }
     return a.stream_kv ? launch_mfma<E, Kv16, D, G, true>(a, st) : launch_mfma<E, Kv16, D, G, false>(a, st);
   }

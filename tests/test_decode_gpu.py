@@ -101,6 +101,21 @@ def test_mha_vector_core_sweep(dtype, D, ps):
     assert torch.equal(shared, out)
 
 
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64)])
+def test_mha_few_long_sequences_queued_partitions(dtype, D):
+    """Fewer than 1024 (sequence, kv head) pairs but long sequences: the
+    library cuts 256-token partitions and feeds the vector-ALU core from the
+    work queue (8 x 40 pairs, up to 8 partitions each), then merges them."""
+    lens = [0, 1, 17, 255, 256, 257, 1999, 2000]
+    wl = W.make_random(zlib.crc32(f"mha-q16-{dtype}-{D}".encode()) % 10000, len(lens), 40, 40, D, dtype, lens,
+                       extra_table_cols=1)
+    assert wl.num_seqs * wl.num_kv_heads < 1024
+    out, _ = gpu_decode(wl, partition_size=0)
+    g = out.double().numpy()
+    assert_parity(g, oracle_decode(wl), dtype, f"MHA {dtype} D={D}, few long sequences, queued partitions")
+    assert (g[0] == 0).all()
+
+
 def test_mha_vector_core_longest_first_order():
     """Without partitions the 16-bit vector-ALU launch first orders the
     sequences by block count (one workgroup: counts, running sums, places).

@@ -151,6 +151,17 @@ def test_fp8_mha_queue_library_partitions():
             assert np.isnan(g[s]).all()
 
 
+def test_fp8_mha_few_long_sequences():
+    """Fewer than 1024 (sequence, kv head) pairs, long sequences: the queued
+    launch with the library's partitions (not the matrix-core split)."""
+    lens = [0, 1, 17, 255, 256, 257, 1999, 2000]
+    wl = W.make_random(911, len(lens), 40, 40, 128, "f16", lens, extra_table_cols=1)
+    kc8, vc8 = _fp8_case(wl, 911)
+    g = _run_fp8(wl, kc8, vc8, 0)
+    assert_parity(g, _ref_fp8(wl, kc8, vc8), "f16", "fp8 MHA few long sequences")
+    assert (g[0] == 0).all()
+
+
 def test_fp8_mha_queue_graph_replays():
     """The queued launch (counter reset, decode, reduce) captured in a HIP graph
     replays to the eager bytes, with eager work between replays."""
