@@ -870,7 +870,8 @@ __device__ inline u32x2 lds_read_tr16(const char* p) {
 // TW = 2 is built (two waves per SIMD); TW = 4 (one wave per SIMD, the
 // accumulators in AGPRs) measured slower.  TPG = 16 (8 waves) for many
 // tiles per (sequence, kv head), TPG = 8 (4 waves, two workgroups per CU)
-// when a (sequence, kv head) has at most 8 tiles, so fewer waves idle.
+// when a (sequence, kv head) has at most 8 tiles, so fewer waves idle; with
+// very few tiles TW = 1, TPG = 4 (4 waves of one tile).
 constexpr int kPfTilesPerWave = 2;
 constexpr int kPfSmallGroupTiles = 8;
 
@@ -907,7 +908,7 @@ pa_prefill_lds_kernel(void* __restrict__ out, const void* __restrict__ query, co
   constexpr int BS = kBlockSize, TPT = 16 / G, KS = SH::kKs, VE = SH::kVe;
   constexpr int WAVES = TPG / TW;
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves per workgroup");
-  static_assert(TW == 2 || TW == 4, "two or four tiles per wave");
+  static_assert(TW == 1 || TW == 2 || TW == 4, "one, two or four tiles per wave");
   constexpr int RP = pf_k_pitch<D>(), VP = pf_v_pitch<D>(), KB = pf_k_bytes<D>(), SB = pf_stage_bytes<D>();
   constexpr int KVB = KV::kBytes;                     // bytes per element in the pools
   constexpr int CPR = D * KVB / 16;                   // 16-byte chunks per pool row

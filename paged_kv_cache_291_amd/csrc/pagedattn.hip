@@ -44,6 +44,8 @@ constexpr int kMfmaQueueHeads = 8;
 // LDS (16 per workgroup); one tile runs one wave per tile (8B batch, 5..8
 // tokens: 391-402 us through LDS, 608-618 us one wave per tile).
 constexpr int kPrefillLdsTiles = 2;
+// Up to this many tiles the many-tile kernel runs one tile per wave.
+constexpr int kPfOneTileWaveTiles = 4;
 
 // ------------------------------------------------------------ scatter kernel
 
@@ -614,6 +616,19 @@ int launch_prefill(void* out, const void* query, const void* kc, const void* vc,
     const long long grid = (pairs + 7) / 8 * 8 * gpp;
     if (grid > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     constexpr int TW = kPfTilesPerWave;
+    if (tiles <= kPfOneTileWaveTiles) {
+      // few tiles: workgroups of 4 waves with one tile each, so that fewer
+      // waves only stage blocks (8B batch, 5 / 8 / 12 / 16 query tokens:
+      // 268.4 / 276.6 / 285.4 / 292.6 us against 274.9 / 282.5 / 292.8 /
+      // 298.6 us with two tiles per wave)
+      auto k1 = nt ? pa_prefill_lds_kernel<E, KV, D, G, true, 1, 4> : pa_prefill_lds_kernel<E, KV, D, G, false, 1, 4>;
+      const long long gpp1 = ceil_div(tiles, 4), grid1 = (pairs + 7) / 8 * 8 * gpp1;
+      if (grid1 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+      hipLaunchKernelGGL(k1, dim3((unsigned)grid1), dim3(256), 0, st, out, query,
+                         static_cast<const char*>(kc), static_cast<const char*>(vc), bt, sl, qs, num_seqs, num_heads,
+                         num_kv_heads, max_blocks, num_blocks, (int)gpp1, qk_scale, v_scale, order);
+      return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+    }
     auto k = tpg == 16 ? (nt ? pa_prefill_lds_kernel<E, KV, D, G, true, TW, 16> : pa_prefill_lds_kernel<E, KV, D, G, false, TW, 16>)
                        : (nt ? pa_prefill_lds_kernel<E, KV, D, G, true, TW, kPfSmallGroupTiles>
                              : pa_prefill_lds_kernel<E, KV, D, G, false, TW, kPfSmallGroupTiles>);
