@@ -8,10 +8,12 @@
 // sequence's table and length, gather K/V from the physical blocks it names,
 // run standard attention, write the output).  The kernels are our own design
 // for 64-lane waves, matrix cores and HBM3E:
-//   decode_mfma.h  bf16/fp16 KV on the matrix cores (fixed partitions, or a
-//                  balanced split of the whole batch over the GPU)
-//   decode_valu.h  fp32 KV, and 16-bit KV without query-head grouping, on
-//                  the vector ALUs
+//   decode_mfma.h  bf16/fp16/fp8 KV on the matrix cores (fixed partitions,
+//                  a balanced split of the whole batch over the GPU, and
+//                  several query tokens per sequence)
+//   decode_valu.h  fp32 KV, and 16-bit or fp8 KV without query-head
+//                  grouping, on the vector ALUs (one workgroup per item, or
+//                  workgroups fed from a work queue)
 //   reduce.h       log-sum-exp merge of partial results
 // The scatter kernel below writes new tokens' K/V rows into their slots.
 
